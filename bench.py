@@ -1,0 +1,261 @@
+"""Bench: MoBA causal prefill on one MI355X.
+
+One step = one whole moba_prefill (pool, gate + top-k, index build, past-
+block attention, own-block attention, merge) over the resident synthetic
+input of the 1M-token workload (batch 1, 32 query / 8 KV heads, d 128, bf16,
+block 4096, top-k 12).  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-dense] [--no-cpu] [--no-secondary]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MoBA prefill tokens/s + attn TFLOP/s (% bf16 MFMA peak) at 128K and 1M tokens")
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MAIN = "moba-1m-gqa32x8-d128"
+SECONDARY = "moba-128k-gqa32x8-d128"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_past_1m_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_moba_amd", "csrc", "attn.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def work_counts(cfg):
+    """Algorithmic work of one prefill (selected-block pairs only)."""
+    B, n, k, d = cfg.block_size, cfg.n_blocks, cfg.topk, cfg.head_dim
+    heads = cfg.hq * cfg.batch
+    past_blocks = sum(min(b, k - 1) for b in range(n)) if k < n else n * (n - 1) // 2
+    past_pairs = B * B * past_blocks * heads
+    own_pairs = n * B * (B + 1) // 2 * heads
+    esz = 2 if cfg.dtype == "bf16" else 4
+    S = cfg.seqlen
+    return {
+        "flops_past": 4.0 * d * past_pairs,
+        "flops_own": 4.0 * d * own_pairs,
+        "flops_total": 4.0 * d * (past_pairs + own_pairs),
+        "flops_dense": 4.0 * d * heads * S * (S + 1) / 2,
+        "pool_bytes": cfg.batch * S * cfg.hkv * d * esz + cfg.batch * cfg.hkv * n * d * 4,
+        "gate_bytes": (cfg.batch * S * cfg.hq * d * esz + cfg.batch * S * cfg.hq * k * 4
+                       + cfg.batch * cfg.hkv * n * d * 4),
+    }
+
+
+def file_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(workload):
+    """HBM bytes per launch of the past-block attention kernel from committed
+    rocprofv3 counter runs, or None when absent or taken on other kernel code."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("attn_src_sha256") != file_hash(ATTN_SRC):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_prefill(moba, torch, cfg, q, k, v, steps, warmup):
+    ws_bytes, _ = moba.moba_workspace_size(cfg.batch, cfg.seqlen, cfg.hq, cfg.hkv,
+                                           cfg.head_dim, cfg.block_size, cfg.topk,
+                                           moba.MOBA_DTYPE_BF16 if cfg.dtype == "bf16"
+                                           else moba.MOBA_DTYPE_FP32)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    for i in range(warmup):
+        moba.moba_prefill(q, k, v, cfg.block_size, cfg.topk, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{warmup} done")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(moba.MOBA_NUM_STAGES + 1)]
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        moba.moba_prefill(q, k, v, cfg.block_size, cfg.topk, out=out, workspace=ws,
+                          stage_events=ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = [0.0] * moba.MOBA_NUM_STAGES
+    for s in range(steps):
+        for i in range(moba.MOBA_NUM_STAGES):
+            stage_ms[i] += ev[s][i].elapsed_time(ev[s][i + 1]) / steps
+    total_ev = sum(ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)) / steps
+    del ws
+    return wall * 1000.0 / steps, total_ev, dict(zip(moba.STAGE_NAMES, stage_ms)), out
+
+
+def time_dense(moba, torch, cfg, q, k, v):
+    """Full causal attention on the same inputs (topk = number of blocks)."""
+    out = torch.empty_like(q)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    moba.moba_prefill(q, k, v, cfg.block_size, cfg.n_blocks, out=out)     # warm-up
+    torch.cuda.synchronize()
+    e0.record()
+    moba.moba_prefill(q, k, v, cfg.block_size, cfg.n_blocks, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def cpu_baseline(cfg, host, n_rows=2048, seed=5):
+    """The fp64 oracle on the host cores: full pool, gate + attention on a
+    random sample of query rows, extrapolated to the whole problem."""
+    import numpy as np
+    import oracle
+    from synth import to_oracle_array
+    qa, code = to_oracle_array(host["q"])
+    ka, _ = to_oracle_array(host["k"])
+    va, _ = to_oracle_array(host["v"])
+    b, S, hq, hkv, d, B, k = (cfg.batch, cfg.seqlen, cfg.hq, cfg.hkv, cfg.head_dim,
+                              cfg.block_size, cfg.topk)
+    rng = np.random.default_rng(seed)
+    rows = np.stack([rng.integers(0, b, n_rows), rng.integers(0, hq, n_rows),
+                     rng.integers(0, S, n_rows)], axis=1).astype(np.int64)
+    t0 = time.perf_counter()
+    kbar = oracle.pool(ka, code, b, S, hkv, d, B)
+    t1 = time.perf_counter()
+    idx, _, _ = oracle.gate(qa, code, kbar, b, S, hq, hkv, d, B, k, rows)
+    oracle.attend(qa, ka, va, code, b, S, hq, hkv, d, B, k, rows, idx)
+    t2 = time.perf_counter()
+    total_rows = b * hq * S
+    est = (t1 - t0) + (t2 - t1) * total_rows / n_rows
+    return {
+        "value": b * S / est,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"full fp64 pool of K ({t1 - t0:.2f} s) + gate and attention of "
+                   f"{n_rows} uniformly random query rows ({t2 - t1:.2f} s), extrapolated "
+                   f"to all {total_rows} rows; {est:.0f} s estimated for the whole prefill"),
+        "measured_s": round(t2 - t0, 3),
+    }
+
+
+def measure(moba, torch, cfg, dev, steps, warmup, dense, want_host):
+    from synth import make_inputs
+    log(f"{cfg.name}: generating inputs on the GPU")
+    inp = make_inputs(cfg, device=dev)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    torch.cuda.synchronize()
+    ms, ms_ev, stages, _ = time_prefill(moba, torch, cfg, q, k, v, steps, warmup)
+    log(f"{cfg.name}: {ms:.2f} ms/step; stages {stages}")
+    res = {"ms": ms, "ms_events": ms_ev, "stages": stages}
+    if dense:
+        torch.cuda.empty_cache()
+        res["dense_ms"] = time_dense(moba, torch, cfg, q, k, v)
+        log(f"{cfg.name}: dense causal {res['dense_ms']:.1f} ms")
+    host = {x: inp[x].cpu() for x in ("q", "k", "v")} if want_host else None
+    del q, k, v, inp
+    torch.cuda.empty_cache()
+    return res, host
+
+
+def summarize(cfg, res):
+    w = work_counts(cfg)
+    st = res["stages"]
+    attn_ms = st["attn_past"] + st["attn_own"] + st["merge"]
+    out = {
+        "ms_per_step": round(res["ms"], 3),
+        "tokens_per_s": cfg.batch * cfg.seqlen / (res["ms"] / 1000.0),
+        "stages_ms": {k: round(v, 3) for k, v in st.items()},
+        "selected_tflop": w["flops_total"] / 1e12,
+        "attn_tflops": w["flops_total"] / (attn_ms / 1000.0) / 1e12,
+        "attn_frac_bf16_peak": w["flops_total"] / (attn_ms / 1000.0) / 1e12 / BF16_PEAK_TFLOPS,
+        "end_to_end_tflops": w["flops_total"] / (res["ms"] / 1000.0) / 1e12,
+        "past_attn_tflops": w["flops_past"] / (st["attn_past"] / 1000.0) / 1e12
+        if st["attn_past"] > 0 else None,
+        "own_attn_tflops": w["flops_own"] / (st["attn_own"] / 1000.0) / 1e12,
+        "pool_gbs": w["pool_bytes"] / (st["pool"] / 1000.0) / 1e9,
+        "pool_frac_hbm_peak": w["pool_bytes"] / (st["pool"] / 1000.0) / 1e9 / HBM_PEAK_GBS,
+        "gate_gbs": w["gate_bytes"] / (st["gate"] / 1000.0) / 1e9,
+        "gate_frac_hbm_peak": w["gate_bytes"] / (st["gate"] / 1000.0) / 1e9 / HBM_PEAK_GBS,
+    }
+    if "dense_ms" in res:
+        out["dense_causal_ms"] = round(res["dense_ms"], 3)
+        out["speedup_vs_dense"] = res["dense_ms"] / res["ms"]
+        out["dense_tflops"] = w["flops_dense"] / (res["dense_ms"] / 1000.0) / 1e12
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=MAIN)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the prefill shards by KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_moba_amd as moba
+    from synth import config_by_name
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    cfg = config_by_name(args.workload)
+    res, host = measure(moba, torch, cfg, dev, args.steps, args.warmup, not args.no_dense,
+                        not args.no_cpu)
+    main_sum = summarize(cfg, res)
+    w = work_counts(cfg)
+    past_ms = res["stages"]["attn_past"]
+    achieved = w["flops_past"] / (past_ms / 1000.0) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": main_sum["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_sum["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Gaussian Q/K/V with planted high-affinity blocks)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seqlen,
+                   "num_q_heads": cfg.hq, "num_kv_heads": cfg.hkv, "head_dim": cfg.head_dim,
+                   "block_size": cfg.block_size, "topk": cfg.topk, "parallelism": "single-gpu"},
+        "roofline": {"kernel": "attn_bf16_kernel<128, PAST> (past-block attention)",
+                     "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                     "traffic": traffic_for(cfg.name),
+                     "avg_launch_ms": round(past_ms, 3)},
+    }
+    line.update({k: v for k, v in main_sum.items() if k not in ("ms_per_step",)})
+    if not args.no_cpu:
+        log("timing the CPU oracle on a row sample")
+        line["cpu_baseline"] = cpu_baseline(cfg, host)
+    host = None
+    if not args.no_secondary and args.workload == MAIN:
+        cfg2 = config_by_name(SECONDARY)
+        res2, _ = measure(moba, torch, cfg2, dev, args.steps, args.warmup, not args.no_dense,
+                          False)
+        line["secondary"] = {"workload": cfg2.name, **summarize(cfg2, res2)}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+"""ctypes binding of libmoba.so (argument marshalling only).
+
+Every step of the MoBA prefill runs in the library's HIP kernels; torch is
+used here only to own device memory and to name the current HIP stream.
+There is no fallback: if libmoba.so is missing or a call fails, an exception
+is raised.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoba.so")
+
+MOBA_OK = 0
+MOBA_ERR_INVALID_ARGUMENT = 1
+MOBA_ERR_UNSUPPORTED = 2
+MOBA_ERR_WORKSPACE_TOO_SMALL = 3
+MOBA_ERR_HIP = 4
+MOBA_DTYPE_BF16 = 0
+MOBA_DTYPE_FP32 = 1
+MOBA_NUM_STAGES = 6
+STAGE_NAMES = ("pool", "gate", "index", "attn_past", "attn_own", "merge")
+EXPORTS = ("moba_abi_version", "moba_status_string", "moba_workspace_size", "moba_pool",
+           "moba_gate", "moba_prefill", "moba_prefill_timed")
+
+
+class MobaError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {moba_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmoba.so with argument types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run "
+                          "`python -m block_sparse_attention_moba_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    ci, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    L.moba_abi_version.restype = ci
+    L.moba_abi_version.argtypes = []
+    L.moba_status_string.restype = ctypes.c_char_p
+    L.moba_status_string.argtypes = [ci]
+    L.moba_workspace_size.restype = ci
+    L.moba_workspace_size.argtypes = [ci] * 8 + [ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.moba_pool.restype = ci
+    L.moba_pool.argtypes = [vp, vp] + [ci] * 6 + [vp, sz, vp]
+    L.moba_gate.restype = ci
+    L.moba_gate.argtypes = [vp, vp, vp] + [ci] * 8 + [vp, sz, vp]
+    L.moba_prefill.restype = ci
+    L.moba_prefill.argtypes = [vp, vp, vp, vp] + [ci] * 8 + [vp, sz, vp]
+    L.moba_prefill_timed.restype = ci
+    L.moba_prefill_timed.argtypes = [vp, vp, vp, vp] + [ci] * 8 + [vp, sz, vp,
+                                                                  ctypes.POINTER(vp)]
+    _lib = L
+    return L
+
+
+def moba_abi_version():
+    return lib().moba_abi_version()
+
+
+def moba_status_string(status):
+    return lib().moba_status_string(int(status)).decode()
+
+
+def _check(status, what):
+    if status != MOBA_OK:
+        raise MobaError(status, what)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return MOBA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return MOBA_DTYPE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def moba_workspace_size(batch, seqlen, num_q_heads, num_kv_heads, head_dim, block_size, topk,
+                        dtype=MOBA_DTYPE_BF16):
+    """(prefill_bytes, gate_bytes) for a problem."""
+    pb, gb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(lib().moba_workspace_size(batch, seqlen, num_q_heads, num_kv_heads, head_dim,
+                                     block_size, topk, dtype, ctypes.byref(pb), ctypes.byref(gb)),
+           "moba_workspace_size")
+    return pb.value, gb.value
+
+
+def _workspace(nbytes, device, workspace):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def moba_pool(k, block_size, workspace=None):
+    """fp32 block means of k [batch, seqlen, hkv, d] -> [batch, hkv, seqlen/block_size, d]."""
+    _need_cuda(k)
+    b, S, hkv, d = k.shape
+    dt = _dtype_code(k)
+    _, gb = moba_workspace_size(b, S, hkv, hkv, d, block_size, 1, dt)
+    ws = _workspace(gb, k.device, workspace)
+    kbar = torch.empty((b, hkv, S // block_size, d), dtype=torch.float32, device=k.device)
+    _check(lib().moba_pool(_ptr(k), _ptr(kbar), b, S, hkv, d, block_size, dt, _ptr(ws),
+                           ws.numel(), _stream()), "moba_pool")
+    return kbar
+
+
+def moba_gate(q, k, block_size, topk, workspace=None):
+    """Selected blocks per query row: int32 [batch, hq, seqlen, topk], ascending, -1 padded."""
+    _need_cuda(q, k)
+    b, S, hq, d = q.shape
+    hkv = k.shape[2]
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype:
+        raise TypeError("q and k must share a dtype")
+    _, gb = moba_workspace_size(b, S, hq, hkv, d, block_size, topk, dt)
+    ws = _workspace(gb, q.device, workspace)
+    idx = torch.empty((b, hq, S, topk), dtype=torch.int32, device=q.device)
+    _check(lib().moba_gate(_ptr(q), _ptr(k), _ptr(idx), b, S, hq, hkv, d, block_size, topk, dt,
+                           _ptr(ws), ws.numel(), _stream()), "moba_gate")
+    return idx
+
+
+def moba_prefill(q, k, v, block_size, topk, out=None, workspace=None, stage_events=None):
+    """MoBA causal prefill forward.  q [b, S, hq, d], k/v [b, S, hkv, d] -> out like q.
+
+    stage_events: optional list of MOBA_NUM_STAGES + 1 torch.cuda.Event(enable_timing=True)
+    recorded around the stages on the current stream.
+    """
+    _need_cuda(q, k, v)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    b, S, hq, d = q.shape
+    hkv = k.shape[2]
+    if k.shape != (b, S, hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [batch, seqlen, num_kv_heads, head_dim]")
+    dt = _dtype_code(q)
+    pb, _ = moba_workspace_size(b, S, hq, hkv, d, block_size, topk, dt)
+    ws = _workspace(pb, q.device, workspace)
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda(out)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), b, S, hq, hkv, d, block_size, topk, dt,
+            _ptr(ws), ws.numel(), _stream())
+    if stage_events is None:
+        _check(lib().moba_prefill(*args), "moba_prefill")
+    else:
+        if len(stage_events) != MOBA_NUM_STAGES + 1:
+            raise ValueError(f"need {MOBA_NUM_STAGES + 1} events")
+        arr = (ctypes.c_void_p * (MOBA_NUM_STAGES + 1))()
+        for i, e in enumerate(stage_events):
+            e.record()          # make sure the HIP event exists before handing it over
+            arr[i] = ctypes.c_void_p(e.cuda_event)
+        _check(lib().moba_prefill_timed(*args, arr), "moba_prefill_timed")
+    return out

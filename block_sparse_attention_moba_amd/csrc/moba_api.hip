@@ -1,0 +1,243 @@
+// C ABI of libmoba.so: argument checks (all before any HIP call), workspace
+// carve-up and the launch sequence of the MoBA prefill stages.
+#include <stdint.h>
+#include <string.h>
+
+#include "moba.h"
+#include "moba_internal.hpp"
+
+using namespace moba;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr long long kMaxSeq = 1ll << 24;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Layout {
+    size_t kbar = 0, poolp = 0, idx = 0, cnt = 0, cursor = 0, list_off = 0, tile_off = 0,
+           lists = 0, part_o = 0, part_lse = 0, total = 0;
+};
+
+// Past selections over all rows: every row in block i keeps min(topk - 1, i) past blocks.
+unsigned long long past_rows(const Problem &p) {
+    unsigned long long per_seq = 0;
+    for (int i = 0; i < p.n; ++i) per_seq += (unsigned long long)min(p.topk - 1, i);
+    return per_seq * (unsigned long long)p.B * p.Hq * p.batch;
+}
+
+size_t elem_size(const Problem &p) { return p.dtype == kBF16 ? 2 : 4; }
+
+moba_status_t make_problem(int batch, int S, int Hq, int Hkv, int D, int B, int topk,
+                           moba_dtype_t dt, Problem *p) {
+    if (batch <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0 || topk <= 0)
+        return MOBA_ERR_INVALID_ARGUMENT;
+    if (Hq % Hkv != 0) return MOBA_ERR_INVALID_ARGUMENT;
+    if (dt != MOBA_DTYPE_BF16 && dt != MOBA_DTYPE_FP32) return MOBA_ERR_INVALID_ARGUMENT;
+    if (D != 64 && D != 128) return MOBA_ERR_UNSUPPORTED;
+    if (B % 64 != 0 || S % B != 0) return MOBA_ERR_UNSUPPORTED;
+    if ((long long)S > kMaxSeq) return MOBA_ERR_UNSUPPORTED;
+    p->batch = batch; p->S = S; p->Hq = Hq; p->Hkv = Hkv; p->D = D; p->B = B; p->topk = topk;
+    p->dtype = (dt == MOBA_DTYPE_BF16) ? kBF16 : kF32;
+    p->G = Hq / Hkv;
+    p->n = S / B;
+    p->dense = topk >= p->n;
+    p->npast = min(topk - 1, p->n - 1);
+    if (!p->dense && p->npast > kMaxPast) return MOBA_ERR_UNSUPPORTED;
+    return MOBA_OK;
+}
+
+Layout gate_layout(const Problem &p) {
+    Layout l;
+    size_t off = 0;
+    const size_t nchunk = p.B / pool_chunk(p.B);
+    l.kbar = off; off += align_up((size_t)p.batch * p.Hkv * p.n * p.D * 4);
+    l.poolp = off; off += align_up((size_t)p.batch * p.Hkv * p.n * nchunk * p.D * 4);
+    l.total = off;
+    return l;
+}
+
+Layout prefill_layout(const Problem &p) {
+    if (p.dense) return Layout();   // full causal attention needs no workspace
+    Layout l = gate_layout(p);
+    size_t off = l.total;
+    const size_t rows = (size_t)p.batch * p.Hq * p.S;
+    const size_t L = (size_t)p.batch * p.Hkv * p.n;
+    l.idx = off; off += align_up(rows * p.topk * 4);
+    l.cnt = off; off += align_up(L * 4);
+    l.cursor = off; off += align_up(L * 4);
+    l.list_off = off; off += align_up((L + 1) * 8);
+    l.tile_off = off; off += align_up((L + 1) * 4);
+    l.lists = off; off += align_up((size_t)past_rows(p) * 8);
+    l.part_o = off; off += align_up(rows * p.topk * p.D * elem_size(p));
+    l.part_lse = off; off += align_up(rows * p.topk * 4);
+    l.total = off;
+    return l;
+}
+
+bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+moba_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOBA_OK : MOBA_ERR_HIP; }
+
+struct Events {
+    void *const *ev;
+    hipStream_t st;
+    hipError_t mark(int i) const {
+        return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), st) : hipSuccess;
+    }
+};
+
+moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *out, int batch,
+                           int S, int Hq, int Hkv, int D, int B, int topk, moba_dtype_t dt,
+                           void *ws, size_t ws_bytes, void *stream, void *const *events) {
+    Problem p;
+    moba_status_t rc = make_problem(batch, S, Hq, Hkv, D, B, topk, dt, &p);
+    if (rc != MOBA_OK) return rc;
+    if (!q || !k || !v || !out) return MOBA_ERR_INVALID_ARGUMENT;
+    const size_t qbytes = (size_t)batch * S * Hq * D * elem_size(p);
+    const size_t kvbytes = (size_t)batch * S * Hkv * D * elem_size(p);
+    if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kvbytes) ||
+        overlaps(out, qbytes, v, kvbytes))
+        return MOBA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return MOBA_ERR_UNSUPPORTED;
+    const Layout l = prefill_layout(p);
+    if (ws_bytes < l.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    if (l.total > 0 && !ws) return MOBA_ERR_INVALID_ARGUMENT;
+    if (ws && !aligned(ws, kAlign)) return MOBA_ERR_UNSUPPORTED;
+
+    hipStream_t st = as_stream(stream);
+    const Events E{events, st};
+    char *w = static_cast<char *>(ws);
+    AttnBuffers bf;
+    bf.q = q; bf.k = k; bf.v = v; bf.out = out;
+    hipError_t e = hipSuccess;
+    if (p.dense) {
+        for (int i = 0; i <= MOBA_STAGE_ATTN_PAST && e == hipSuccess; ++i) e = E.mark(i);
+        if (e == hipSuccess) e = launch_attn_dense(bf, p, st);
+        for (int i = MOBA_STAGE_ATTN_OWN; i <= MOBA_NUM_STAGES && e == hipSuccess; ++i) e = E.mark(i);
+        return hip_status(e);
+    }
+    float *kbar = reinterpret_cast<float *>(w + l.kbar);
+    float *poolp = reinterpret_cast<float *>(w + l.poolp);
+    int32_t *idx = reinterpret_cast<int32_t *>(w + l.idx);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(w + l.cnt);
+    uint32_t *cursor = reinterpret_cast<uint32_t *>(w + l.cursor);
+    uint64_t *list_off = reinterpret_cast<uint64_t *>(w + l.list_off);
+    uint32_t *tile_off = reinterpret_cast<uint32_t *>(w + l.tile_off);
+    uint64_t *lists = reinterpret_cast<uint64_t *>(w + l.lists);
+    bf.part_o = w + l.part_o;
+    bf.part_lse = reinterpret_cast<float *>(w + l.part_lse);
+    bf.lists = lists; bf.list_off = list_off; bf.tile_off = tile_off;
+
+    const unsigned long long prow = past_rows(p);
+    const unsigned long long L = (unsigned long long)p.batch * p.Hkv * p.n;
+    const unsigned long long tiles_upper = (prow + kTileRows - 1) / kTileRows + L;
+
+    if ((e = E.mark(MOBA_STAGE_POOL)) != hipSuccess) return MOBA_ERR_HIP;
+    if ((e = launch_pool(k, kbar, poolp, p, st)) != hipSuccess) return MOBA_ERR_HIP;
+    if ((e = E.mark(MOBA_STAGE_GATE)) != hipSuccess) return MOBA_ERR_HIP;
+    if ((e = launch_gate(q, kbar, idx, p, st)) != hipSuccess) return MOBA_ERR_HIP;
+    if ((e = E.mark(MOBA_STAGE_INDEX)) != hipSuccess) return MOBA_ERR_HIP;
+    if (prow > 0 &&
+        (e = launch_index(idx, cnt, cursor, list_off, tile_off, lists, p, st)) != hipSuccess)
+        return MOBA_ERR_HIP;
+    if ((e = E.mark(MOBA_STAGE_ATTN_PAST)) != hipSuccess) return MOBA_ERR_HIP;
+    if (prow > 0 && (e = launch_attn_past(bf, p, tiles_upper, st)) != hipSuccess)
+        return MOBA_ERR_HIP;
+    if ((e = E.mark(MOBA_STAGE_ATTN_OWN)) != hipSuccess) return MOBA_ERR_HIP;
+    if ((e = launch_attn_own(bf, p, st)) != hipSuccess) return MOBA_ERR_HIP;
+    if ((e = E.mark(MOBA_STAGE_MERGE)) != hipSuccess) return MOBA_ERR_HIP;
+    if ((e = launch_merge(bf, p, st)) != hipSuccess) return MOBA_ERR_HIP;
+    if ((e = E.mark(MOBA_NUM_STAGES)) != hipSuccess) return MOBA_ERR_HIP;
+    return MOBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moba_abi_version(void) { return MOBA_ABI_VERSION; }
+
+const char *moba_status_string(moba_status_t s) {
+    switch (s) {
+    case MOBA_OK: return "ok";
+    case MOBA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOBA_ERR_UNSUPPORTED: return "unsupported shape, alignment or dtype";
+    case MOBA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOBA_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+moba_status_t moba_workspace_size(int batch, int S, int Hq, int Hkv, int D, int B, int topk,
+                                  moba_dtype_t dt, size_t *prefill_bytes, size_t *gate_bytes) {
+    Problem p;
+    const moba_status_t rc = make_problem(batch, S, Hq, Hkv, D, B, topk, dt, &p);
+    if (rc != MOBA_OK) return rc;
+    if (prefill_bytes) *prefill_bytes = prefill_layout(p).total;
+    if (gate_bytes) *gate_bytes = gate_layout(p).total;
+    return MOBA_OK;
+}
+
+moba_status_t moba_pool(const void *k, float *kbar, int batch, int S, int Hkv, int D, int B,
+                        moba_dtype_t dt, void *ws, size_t ws_bytes, void *stream) {
+    Problem p;
+    const moba_status_t rc = make_problem(batch, S, Hkv, Hkv, D, B, 1, dt, &p);
+    if (rc != MOBA_OK) return rc;
+    if (!k || !kbar || !ws) return MOBA_ERR_INVALID_ARGUMENT;
+    if (!aligned(k, 16) || !aligned(kbar, 4) || !aligned(ws, kAlign)) return MOBA_ERR_UNSUPPORTED;
+    const Layout l = gate_layout(p);
+    if (ws_bytes < l.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    char *w = static_cast<char *>(ws);
+    return hip_status(
+        launch_pool(k, kbar, reinterpret_cast<float *>(w + l.poolp), p, as_stream(stream)));
+}
+
+moba_status_t moba_gate(const void *q, const void *k, int32_t *block_idx, int batch, int S,
+                        int Hq, int Hkv, int D, int B, int topk, moba_dtype_t dt, void *ws,
+                        size_t ws_bytes, void *stream) {
+    Problem p;
+    const moba_status_t rc = make_problem(batch, S, Hq, Hkv, D, B, topk, dt, &p);
+    if (rc != MOBA_OK) return rc;
+    if (!q || !k || !block_idx || !ws) return MOBA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(block_idx, 4) || !aligned(ws, kAlign))
+        return MOBA_ERR_UNSUPPORTED;
+    const Layout l = gate_layout(p);
+    if (ws_bytes < l.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t st = as_stream(stream);
+    char *w = static_cast<char *>(ws);
+    float *kbar = reinterpret_cast<float *>(w + l.kbar);
+    hipError_t e = hipSuccess;
+    if (!p.dense) e = launch_pool(k, kbar, reinterpret_cast<float *>(w + l.poolp), p, st);
+    if (e == hipSuccess) e = launch_gate(q, kbar, block_idx, p, st);
+    return hip_status(e);
+}
+
+moba_status_t moba_prefill(const void *q, const void *k, const void *v, void *out, int batch,
+                           int S, int Hq, int Hkv, int D, int B, int topk, moba_dtype_t dt,
+                           void *ws, size_t ws_bytes, void *stream) {
+    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, ws, ws_bytes, stream,
+                        nullptr);
+}
+
+moba_status_t moba_prefill_timed(const void *q, const void *k, const void *v, void *out,
+                                 int batch, int S, int Hq, int Hkv, int D, int B, int topk,
+                                 moba_dtype_t dt, void *ws, size_t ws_bytes, void *stream,
+                                 void *const *stage_events) {
+    if (!stage_events) return MOBA_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i <= MOBA_NUM_STAGES; ++i)
+        if (!stage_events[i]) return MOBA_ERR_INVALID_ARGUMENT;
+    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, ws, ws_bytes, stream,
+                        stage_events);
+}
+
+}  // extern "C"

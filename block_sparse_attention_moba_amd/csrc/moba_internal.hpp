@@ -1,0 +1,69 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moba {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Query rows per attention tile (4 waves x 32 rows for bf16; 128 threads x 1 row for fp32).
+constexpr int kTileRows = 128;
+// Largest number of past blocks the gate keeps per row.
+constexpr int kMaxPast = 31;
+// Block-count limit for the LDS histograms of the index build.
+constexpr int kHistMax = 4096;
+
+enum DType { kBF16 = 0, kF32 = 1 };
+
+// Packed row record of the per-(KV head, block) lists: token | head-in-group | slot.
+__host__ __device__ inline uint64_t pack_row(uint32_t t, uint32_t hh, uint32_t slot) {
+    return (uint64_t)t | ((uint64_t)hh << 32) | ((uint64_t)slot << 48);
+}
+__host__ __device__ inline uint32_t row_t(uint64_t r) { return (uint32_t)(r & 0xffffffffu); }
+__host__ __device__ inline uint32_t row_hh(uint64_t r) { return (uint32_t)((r >> 32) & 0xffffu); }
+__host__ __device__ inline uint32_t row_slot(uint64_t r) { return (uint32_t)(r >> 48); }
+
+struct Problem {
+    int batch, S, Hq, Hkv, D, B, topk, dtype;
+    int G;       // Hq / Hkv
+    int n;       // S / B
+    int npast;   // topk - 1 capped at n - 1
+    bool dense;  // topk >= n: plain causal attention
+};
+
+// Map a workgroup index to a tile so that consecutive tiles run on the same
+// XCD (workgroups are dispatched to the 8 XCDs round-robin).  nb % 8 == 0.
+__device__ inline uint32_t xcd_tile(uint32_t bid, uint32_t nb) {
+    return (bid & 7u) * (nb >> 3) + (bid >> 3);
+}
+
+// ---- launchers (each returns the launch status) ----
+hipError_t launch_pool(const void *k, float *kbar, float *partial, const Problem &p,
+                       hipStream_t st);
+hipError_t launch_gate(const void *q, const float *kbar, int32_t *idx, const Problem &p,
+                       hipStream_t st);
+hipError_t launch_index(const int32_t *idx, uint32_t *cnt, uint32_t *cursor, uint64_t *list_off,
+                        uint32_t *tile_off, uint64_t *lists, const Problem &p, hipStream_t st);
+
+struct AttnBuffers {
+    const void *q, *k, *v;
+    void *out;
+    void *part_o;           // [row][topk][D], dtype-sized elements
+    float *part_lse;        // [row][topk], base-2 log-sum-exp of the scaled logits
+    const uint64_t *lists;
+    const uint64_t *list_off;
+    const uint32_t *tile_off;
+};
+hipError_t launch_attn_past(const AttnBuffers &b, const Problem &p, uint64_t tiles_upper,
+                            hipStream_t st);
+hipError_t launch_attn_own(const AttnBuffers &b, const Problem &p, hipStream_t st);
+hipError_t launch_attn_dense(const AttnBuffers &b, const Problem &p, hipStream_t st);
+hipError_t launch_merge(const AttnBuffers &b, const Problem &p, hipStream_t st);
+
+// Pool partial-sum chunk length (tokens) for a block size that is a multiple of 64.
+inline int pool_chunk(int B) { return (B % 256 == 0) ? 256 : (B % 128 == 0 ? 128 : 64); }
+
+}  // namespace moba

@@ -1,0 +1,106 @@
+// Block means of the keys (the "aggregated representation of the block keys"
+// the gate compares each query with; Taiwan AI overview of MoBA, section
+// "技術細節與優勢").
+//
+// Two launches.  pool_partial: one workgroup per (chunk of CT tokens, block,
+// KV head, batch) streams CT x D keys with 16-byte loads (one D-row per
+// D/8 lanes, so a wave reads 64 x 16 contiguous bytes per step) and writes
+// the chunk's fp32 column sums.  pool_finalize: sums the chunk partials of a
+// block in a fixed order and divides by the block size.  No atomics, so the
+// result is bitwise reproducible.
+#include "moba_internal.hpp"
+
+namespace moba {
+
+__device__ inline void load8(const __bf16 *p, float *f) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(w[e] << 16);
+        f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+
+__device__ inline void load8(const float *p, float *f) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// grid (nchunk, n * Hkv, batch), 256 threads.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_partial_kernel(const T *__restrict__ k,
+                                                           float *__restrict__ partial, int S,
+                                                           int Hkv, int B, int n, int CT) {
+    constexpr int LPT = D / 8;       // lanes per token row
+    constexpr int TPP = 256 / LPT;   // token rows per pass
+    __shared__ float red[TPP][D + 1];
+    const int chunk = blockIdx.x;
+    const int j = blockIdx.y / Hkv;
+    const int g = blockIdx.y % Hkv;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int vec = tid % LPT;
+    const int tr = tid / LPT;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const int t0 = j * B + chunk * CT;
+    for (int t = t0 + tr; t < t0 + CT; t += TPP) {
+        float f[8];
+        load8(k + (((size_t)b * S + t) * Hkv + g) * D + vec * 8, f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += f[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[tr][vec * 8 + e] = acc[e];
+    __syncthreads();
+    if (tid < D) {
+        float s = 0.f;
+        for (int r = 0; r < TPP; ++r) s += red[r][tid];
+        const int nchunk = gridDim.x;
+        partial[((((size_t)b * Hkv + g) * n + j) * nchunk + chunk) * D + tid] = s;
+    }
+}
+
+// grid (ceil(batch * Hkv * n * D / 256)), 256 threads: one output element each.
+__global__ __launch_bounds__(256) void pool_finalize_kernel(const float *__restrict__ partial,
+                                                            float *__restrict__ kbar,
+                                                            long long total, int D, int nchunk,
+                                                            int B) {
+    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= total) return;
+    const long long blk = e / D;
+    const int i = (int)(e % D);
+    const float *src = partial + (size_t)blk * nchunk * D + i;
+    float s = 0.f;
+    for (int c = 0; c < nchunk; ++c) s += src[(size_t)c * D];
+    kbar[e] = s / (float)B;
+}
+
+template <typename T, int D>
+static hipError_t pool_impl(const void *k, float *kbar, float *partial, const Problem &p,
+                            hipStream_t st) {
+    const int CT = pool_chunk(p.B);
+    const int nchunk = p.B / CT;
+    dim3 grid(nchunk, p.n * p.Hkv, p.batch);
+    pool_partial_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T *>(k), partial, p.S,
+                                                    p.Hkv, p.B, p.n, CT);
+    const long long total = (long long)p.batch * p.Hkv * p.n * D;
+    pool_finalize_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(partial, kbar, total, D,
+                                                                         nchunk, p.B);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool(const void *k, float *kbar, float *partial, const Problem &p,
+                       hipStream_t st) {
+    if (p.dtype == kBF16)
+        return p.D == 64 ? pool_impl<__bf16, 64>(k, kbar, partial, p, st)
+                         : pool_impl<__bf16, 128>(k, kbar, partial, p, st);
+    return p.D == 64 ? pool_impl<float, 64>(k, kbar, partial, p, st)
+                     : pool_impl<float, 128>(k, kbar, partial, p, st);
+}
+
+}  // namespace moba

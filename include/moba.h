@@ -1,0 +1,155 @@
+/*
+ * moba.h -- MoBA (Mixture of Block Attention) causal prefill forward on one
+ * AMD Instinct MI355X (gfx950).  C ABI of libmoba.so.
+ *
+ * The operation.  MoBA splits the context into blocks of `block_size`
+ * tokens and routes every query token to a few blocks with a parameter-free
+ * top-k gate; attention then runs over the tokens of the chosen blocks only
+ * (MoBA tech-report write-up, section "MoBA：將MoE原理應用于注意力機制": the
+ * list of MoBA's parts and the five implementation steps).  The gate scores
+ * a query against an aggregated representation of each block's keys; the
+ * block holding the query is always chosen and no token attends to a future
+ * position (Taiwan AI overview, section "技術細節與優勢").  Partial results of
+ * the current block and the history blocks are merged by an online softmax
+ * (write-up, the fifth implementation step).  With every causal block
+ * selected the result is full causal attention (the seamless full / sparse
+ * switch the write-up and the overview describe).
+ *
+ * Readings fixed by this library where the pages are silent:
+ *   - block key = mean of the block's keys (fp32);
+ *   - gate score = <q, mean key>, unscaled, for past blocks j < t / block_size;
+ *   - `topk` counts the own block: a query uses its own block plus the
+ *     min(topk - 1, t / block_size) best-scoring past blocks; ties go to the
+ *     smaller block index;
+ *   - softmax scale 1 / sqrt(head_dim); query head h uses KV head
+ *     h / (num_q_heads / num_kv_heads).
+ *
+ * Layouts (all contiguous, head_dim innermost, element type = `dtype`):
+ *   q, out  [batch][seqlen][num_q_heads][head_dim]
+ *   k, v    [batch][seqlen][num_kv_heads][head_dim]
+ *   block_idx (int32) [batch][num_q_heads][seqlen][topk]: the selected
+ *           blocks of each query row, ascending, own block included (it is
+ *           the last valid entry), then -1 padding.
+ *   kbar (fp32) [batch][num_kv_heads][seqlen / block_size][head_dim].
+ *
+ * Ownership.  Every pointer is caller-owned device memory.  The library
+ * allocates nothing, keeps no state between calls and is reentrant: calls on
+ * different streams with different workspaces may run concurrently.  Outputs
+ * are fully overwritten.  `out` must not overlap q, k or v.
+ *
+ * Errors.  The return code is the only channel.  All argument checks run
+ * before any HIP call.  Work is asynchronous on `stream` (a hipStream_t; NULL
+ * is the default stream): results are valid once the caller synchronises the
+ * stream, and a later device error is reported by the caller's next HIP call.
+ *   MOBA_ERR_INVALID_ARGUMENT   null pointer, a size <= 0, num_q_heads not a
+ *                               multiple of num_kv_heads, unknown dtype,
+ *                               `out` overlapping an input;
+ *   MOBA_ERR_UNSUPPORTED        head_dim not 64 or 128; seqlen not a multiple
+ *                               of block_size; block_size not a multiple of
+ *                               64; seqlen > 2^24; topk > 32 while topk <
+ *                               seqlen / block_size; a pointer not 16-byte
+ *                               aligned;
+ *   MOBA_ERR_WORKSPACE_TOO_SMALL  workspace_bytes below moba_workspace_size;
+ *   MOBA_ERR_HIP                a kernel launch was rejected.
+ */
+#ifndef MOBA_H
+#define MOBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOBA_ABI_VERSION 1
+
+typedef enum {
+    MOBA_OK = 0,
+    MOBA_ERR_INVALID_ARGUMENT = 1,
+    MOBA_ERR_UNSUPPORTED = 2,
+    MOBA_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOBA_ERR_HIP = 4
+} moba_status_t;
+
+typedef enum { MOBA_DTYPE_BF16 = 0, MOBA_DTYPE_FP32 = 1 } moba_dtype_t;
+
+/* Stages of moba_prefill, in launch order (for moba_prefill_timed). */
+enum {
+    MOBA_STAGE_POOL = 0,     /* block means of K                                  */
+    MOBA_STAGE_GATE = 1,     /* gate scores + causal top-k                        */
+    MOBA_STAGE_INDEX = 2,    /* per-(KV head, block) lists of the query rows      */
+    MOBA_STAGE_ATTN_PAST = 3,/* attention of listed rows over one past block each */
+    MOBA_STAGE_ATTN_OWN = 4, /* causal attention over each query's own block      */
+    MOBA_STAGE_MERGE = 5,    /* online-softmax merge of the partial outputs       */
+    MOBA_NUM_STAGES = 6
+};
+
+/* ABI version of the loaded library (MOBA_ABI_VERSION at build time). */
+int moba_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *moba_status_string(moba_status_t status);
+
+/*
+ * Workspace bytes needed by moba_prefill (*prefill_bytes) and by moba_gate /
+ * moba_pool (*gate_bytes) for this problem.  Either output pointer may be
+ * NULL.  Host-only; validates like the calls it sizes.
+ */
+moba_status_t moba_workspace_size(int batch, int seqlen, int num_q_heads, int num_kv_heads,
+                                  int head_dim, int block_size, int topk, moba_dtype_t dtype,
+                                  size_t *prefill_bytes, size_t *gate_bytes);
+
+/*
+ * Block means of the keys: kbar[b][g][j][:] = mean of k[b][t][g][:] over the
+ * block_size tokens t of block j, accumulated in fp32 (the "aggregated
+ * representation of the block keys" of the overview, section "技術細節與優勢").
+ * Workspace: at least *gate_bytes of moba_workspace_size.
+ */
+moba_status_t moba_pool(const void *k, float *kbar, int batch, int seqlen, int num_kv_heads,
+                        int head_dim, int block_size, moba_dtype_t dtype, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
+ * Gate and causal top-k (write-up, the first implementation step: assign
+ * query tokens to KV blocks from the gate and the causal mask).  Writes
+ * block_idx as laid out above.  Gate scores are fp32 inner products of the
+ * query with the fp32 block means.  Workspace: at least *gate_bytes.
+ */
+moba_status_t moba_gate(const void *q, const void *k, int32_t *block_idx, int batch, int seqlen,
+                        int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                        int topk, moba_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/*
+ * Whole MoBA causal prefill forward: out = softmax attention of each query
+ * over the tokens t' <= t of its selected blocks.  topk >= seqlen /
+ * block_size gives exact full causal attention (no gating is run).
+ * bf16 inputs: scores and softmax in fp32, P and V products in bf16 on the
+ * matrix cores with fp32 accumulation, partial outputs kept in bf16, output
+ * rounded to bf16 (nearest even).  fp32 inputs: fp32 throughout.
+ * Workspace: at least *prefill_bytes.
+ */
+moba_status_t moba_prefill(const void *q, const void *k, const void *v, void *out, int batch,
+                           int seqlen, int num_q_heads, int num_kv_heads, int head_dim,
+                           int block_size, int topk, moba_dtype_t dtype, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
+ * moba_prefill that also records caller-created hipEvent_t handles on
+ * `stream`: stage_events[s] just before stage s (MOBA_STAGE_*) and
+ * stage_events[MOBA_NUM_STAGES] after the last stage; stages that a problem
+ * does not need record back-to-back events.  stage_events must hold
+ * MOBA_NUM_STAGES + 1 valid events.
+ */
+moba_status_t moba_prefill_timed(const void *q, const void *k, const void *v, void *out,
+                                 int batch, int seqlen, int num_q_heads, int num_kv_heads,
+                                 int head_dim, int block_size, int topk, moba_dtype_t dtype,
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 void *const *stage_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOBA_H */

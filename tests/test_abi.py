@@ -1,0 +1,125 @@
+"""libmoba.so loads, exports what include/moba.h declares, and rejects bad
+arguments before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_moba_amd as moba
+from block_sparse_attention_moba_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moba.h")
+INV, UNS, WS = (_lib.MOBA_ERR_INVALID_ARGUMENT, _lib.MOBA_ERR_UNSUPPORTED,
+                _lib.MOBA_ERR_WORKSPACE_TOO_SMALL)
+BF16, F32 = _lib.MOBA_DTYPE_BF16, _lib.MOBA_DTYPE_FP32
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moba_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = moba.lib()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define\s+MOBA_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert moba.moba_abi_version() == int(m.group(1))
+
+
+def test_status_strings():
+    for s in range(5):
+        assert moba.moba_status_string(s)
+    assert moba.moba_status_string(99) == "unknown status"
+
+
+def ws_size(*args):
+    pb, gb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    rc = moba.lib().moba_workspace_size(*args, ctypes.byref(pb), ctypes.byref(gb))
+    return rc, pb.value, gb.value
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 1024, 2, 2, 64, 128, 3, BF16), INV),        # batch 0
+    ((1, 1024, 3, 2, 64, 128, 3, BF16), INV),        # Hq % Hkv
+    ((1, 1024, 2, 2, 64, 128, 0, BF16), INV),        # topk 0
+    ((1, 1024, 2, 2, 64, 128, 3, 7), INV),           # dtype
+    ((1, 1024, 2, 2, 96, 128, 3, BF16), UNS),        # head_dim
+    ((1, 1000, 2, 2, 64, 128, 3, BF16), UNS),        # S % block
+    ((1, 1024, 2, 2, 64, 32, 3, BF16), UNS),         # block % 64
+    ((1, 1 << 25, 2, 2, 64, 4096, 3, BF16), UNS),    # seqlen limit
+    ((1, 64 * 64, 2, 2, 64, 64, 40, BF16), UNS),     # topk > 32 while sparse
+])
+def test_workspace_size_validation(args, code):
+    rc, _, _ = ws_size(*args)
+    assert rc == code
+
+
+def test_workspace_sizes():
+    rc, pb, gb = ws_size(1, 1024, 2, 2, 64, 128, 3, F32)
+    assert rc == 0 and pb > gb > 0
+    rc, pb, gb = ws_size(1, 1024, 2, 2, 64, 128, 8, F32)   # topk >= n: full attention
+    assert rc == 0 and pb == 0
+    rc, pb2, _ = ws_size(1, 64 * 64, 2, 2, 64, 64, 40 + 24, BF16)
+    assert rc == 0 and pb2 == 0                              # dense again: no topk limit
+    # the 1M-token workload fits one 288 GB GPU with its inputs
+    rc, pb, _ = ws_size(1, 1 << 20, 32, 8, 128, 4096, 12, BF16)
+    assert rc == 0 and 50e9 < pb < 200e9
+
+
+FAKE = 1 << 40          # aligned, never dereferenced: every call below fails validation
+
+
+def prefill(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), out=FAKE + (3 << 32),
+            dims=(1, 1024, 2, 2, 64, 128, 3, BF16), ws=FAKE + (4 << 32), nbytes=1 << 40):
+    vp = ctypes.c_void_p
+    return moba.lib().moba_prefill(vp(q), vp(k), vp(v), vp(out), *dims, vp(ws), nbytes, None)
+
+
+def test_prefill_rejects_before_any_hip_call():
+    assert prefill(q=0) == INV
+    assert prefill(out=0) == INV
+    assert prefill(dims=(1, 1024, 2, 2, 80, 128, 3, BF16)) == UNS
+    assert prefill(q=FAKE + 2) == UNS                        # misaligned
+    assert prefill(out=FAKE + 64) == INV                     # out overlaps q
+    assert prefill(nbytes=16) == WS
+    assert prefill(ws=0) == INV
+    assert prefill(ws=FAKE + (4 << 32) + 16) == UNS          # workspace alignment
+
+
+def test_timed_prefill_needs_events():
+    vp = ctypes.c_void_p
+    arr = (vp * (_lib.MOBA_NUM_STAGES + 1))()
+    rc = moba.lib().moba_prefill_timed(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE + (3 << 32)),
+                                       1, 1024, 2, 2, 64, 128, 3, BF16, vp(FAKE), 1 << 40, None,
+                                       arr)
+    assert rc == INV
+
+
+def test_gate_and_pool_validation():
+    vp = ctypes.c_void_p
+    L = moba.lib()
+    assert L.moba_gate(vp(0), vp(FAKE), vp(FAKE), 1, 1024, 2, 2, 64, 128, 3, BF16, vp(FAKE),
+                       1 << 40, None) == INV
+    assert L.moba_gate(vp(FAKE), vp(FAKE), vp(FAKE + 2), 1, 1024, 2, 2, 64, 128, 3, BF16,
+                       vp(FAKE), 1 << 40, None) == UNS
+    assert L.moba_gate(vp(FAKE), vp(FAKE), vp(FAKE), 1, 1024, 2, 2, 64, 128, 3, BF16,
+                       vp(FAKE), 8, None) == WS
+    assert L.moba_pool(vp(FAKE), vp(0), 1, 1024, 2, 64, 128, BF16, vp(FAKE), 1 << 40,
+                       None) == INV
+    assert L.moba_pool(vp(FAKE), vp(FAKE), 1, 1024, 2, 64, 100, BF16, vp(FAKE), 1 << 40,
+                       None) == UNS
+
+
+def test_python_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 128, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        moba.moba_prefill(q, q[:, :, :1], q[:, :, :1], 64, 2)
