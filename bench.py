@@ -201,6 +201,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -215,6 +217,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        x = torch.ones(1 << 28, dtype=torch.float32, device=dev)    # 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4,
+                          "launches": 3}), flush=True)
+        return
     cfg = config_by_name(args.workload)
     res, host = measure(moba, torch, cfg, dev, args.steps, args.warmup, not args.no_dense,
                         not args.no_cpu)
