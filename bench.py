@@ -168,7 +168,7 @@ def measure(moba, torch, cfg, dev, steps, warmup, dense, want_host):
 def summarize(cfg, res):
     w = work_counts(cfg)
     st = res["stages"]
-    attn_ms = st["attn_past"] + st["attn_own"] + st["merge"]
+    attn_ms = st["attn_past"] + st["attn_own_merge"]
     out = {
         "ms_per_step": round(res["ms"], 3),
         "tokens_per_s": cfg.batch * cfg.seqlen / (res["ms"] / 1000.0),
@@ -179,7 +179,7 @@ def summarize(cfg, res):
         "end_to_end_tflops": w["flops_total"] / (res["ms"] / 1000.0) / 1e12,
         "past_attn_tflops": w["flops_past"] / (st["attn_past"] / 1000.0) / 1e12
         if st["attn_past"] > 0 else None,
-        "own_attn_tflops": w["flops_own"] / (st["attn_own"] / 1000.0) / 1e12,
+        "own_attn_merge_tflops": w["flops_own"] / (st["attn_own_merge"] / 1000.0) / 1e12,
         "pool_gbs": w["pool_bytes"] / (st["pool"] / 1000.0) / 1e9,
         "pool_frac_hbm_peak": w["pool_bytes"] / (st["pool"] / 1000.0) / 1e9 / HBM_PEAK_GBS,
         "gate_gbs": w["gate_bytes"] / (st["gate"] / 1000.0) / 1e9,

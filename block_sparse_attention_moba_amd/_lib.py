@@ -20,8 +20,8 @@ MOBA_ERR_WORKSPACE_TOO_SMALL = 3
 MOBA_ERR_HIP = 4
 MOBA_DTYPE_BF16 = 0
 MOBA_DTYPE_FP32 = 1
-MOBA_NUM_STAGES = 6
-STAGE_NAMES = ("pool", "gate", "index", "attn_past", "attn_own", "merge")
+MOBA_NUM_STAGES = 5
+STAGE_NAMES = ("pool", "gate", "index", "attn_past", "attn_own_merge")
 EXPORTS = ("moba_abi_version", "moba_status_string", "moba_workspace_size", "moba_pool",
            "moba_gate", "moba_prefill", "moba_prefill_timed")
 

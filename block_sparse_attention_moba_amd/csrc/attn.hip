@@ -1,10 +1,10 @@
-// Block-sparse attention over the selected KV blocks, and the online-softmax
-// merge of the partial outputs (write-up "MoBA: Mixture of Block Attention",
-// implementation steps three to five: per-KV-block attention of the queries
-// assigned to it, outputs put back in query order, and an online-softmax
-// merge because a query attends its current block plus several history
-// blocks; Taiwan AI overview, section "技術細節與優勢": the own block is
-// always attended, causally).
+// Block-sparse attention over the selected KV blocks, with the online-softmax
+// merge of the partial outputs fused into the own-block pass (write-up "MoBA:
+// Mixture of Block Attention", implementation steps three to five: per-KV-
+// block attention of the queries assigned to it, outputs put back in query
+// order, and an online-softmax merge because a query attends its current
+// block plus several history blocks; Taiwan AI overview, section
+// "技術細節與優勢": the own block is always attended, causally).
 //
 // Three tile kinds share one kernel body:
 //   PAST  : up to 128 listed query rows of one (batch, KV head, past block j)
@@ -12,8 +12,9 @@
 //           normalised partial output plus its base-2 log-sum-exp to the
 //           row's slot of the partial buffer;
 //   OWN   : 128 consecutive query rows of one head attend their own block
-//           causally (mask only on the sub-tiles that cross the diagonal) and
-//           write the own slot;
+//           causally (mask only on the sub-tiles that cross the diagonal),
+//           then merge with the row's past-block partials and write the
+//           final output;
 //   DENSE : 128 consecutive query rows attend every key <= t and write the
 //           final output (full causal attention, used when every causal block
 //           is selected).
@@ -25,7 +26,11 @@
 // read from K rows whose index has bits 2 and 3 swapped, which makes the 8
 // P values each lane feeds to the PV product 8 consecutive keys; V is stored
 // transposed in LDS (register transpose on the way in) so that the V^T
-// operand is one 16-byte LDS read.
+// operand is one 16-byte LDS read.  The running maximum is only moved (and O
+// rescaled) when a row's new maximum exceeds it by more than 2^8, which
+// keeps every exponent <= 2^8 and skips almost all rescales.  Results leave
+// through LDS so that every global store writes whole 16-byte pieces of
+// contiguous 256-byte rows.
 #include <math.h>
 
 #include "moba_internal.hpp"
@@ -34,8 +39,9 @@ namespace moba {
 
 enum Mode { kPast = 0, kOwn = 1, kDense = 2 };
 
-constexpr int kN = 64;      // keys per sub-tile
-constexpr int kPad = 8;     // LDS row padding (elements) against bank conflicts
+constexpr int kN = 64;                // keys per sub-tile
+constexpr int kPad = 8;               // LDS row padding (elements) against bank conflicts
+constexpr float kRescaleSlack = 8.f;  // log2 units a row max may exceed the running max
 
 struct AttnArgs {
     const void *q, *k, *v;
@@ -44,23 +50,22 @@ struct AttnArgs {
     float *part_lse;
     const uint64_t *lists, *list_off;
     const uint32_t *tile_off;
-    int batch, S, Hq, Hkv, G, B, n, topk;
+    int batch, S, Hq, Hkv, G, B, n, topk, nslot;
     long long L;           // number of lists
     unsigned ntiles;       // tiles of OWN / DENSE launches
     float scale_log2;      // log2(e) / sqrt(D)
 };
 
-// Rows of one tile, as seen by one thread (row index r inside the tile).
 struct Tile {
     int b, g;
     int key_begin;   // first key of the range
     int nsub;        // sub-tiles of kN keys to visit
-    int tmin, tmax;  // token range of the tile's rows (OWN / DENSE)
+    int tmax;        // last token of the tile's rows (OWN / DENSE)
     // PAST
     uint64_t row_begin;
     int nrows;
-    // OWN / DENSE
-    int t0, h, slot, tend;   // rows t0 + r for t0 + r < tend
+    // OWN / DENSE: rows t0 + r for t0 + r < tend
+    int t0, h, tend, npast;
 };
 
 __device__ inline bool decode_tile(const AttnArgs &a, int mode, Tile &tl) {
@@ -83,7 +88,6 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, Tile &tl) {
         tl.nrows = (int)min((uint64_t)kTileRows, rend - tl.row_begin);
         tl.key_begin = j * a.B;
         tl.nsub = a.B / kN;
-        tl.tmin = 0x7fffffff;
         tl.tmax = 0x7fffffff;
         return true;
     }
@@ -100,7 +104,7 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, Tile &tl) {
         tl.t0 = i * a.B + tt * kTileRows;
         tl.tend = i * a.B + a.B;
         tl.key_begin = i * a.B;
-        tl.slot = min(a.topk, i + 1) - 1;
+        tl.npast = min(a.topk - 1, i);
     } else {
         const int ntt = (a.S + kTileRows - 1) / kTileRows;
         const int bh = tile % (a.batch * a.Hq);
@@ -111,9 +115,8 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, Tile &tl) {
         tl.t0 = tt * kTileRows;
         tl.tend = a.S;
         tl.key_begin = 0;
-        tl.slot = 0;
+        tl.npast = 0;
     }
-    tl.tmin = tl.t0;
     tl.tmax = min(tl.t0 + kTileRows, tl.tend) - 1;
     tl.nsub = (tl.tmax - tl.key_begin) / kN + 1;
     return true;
@@ -127,81 +130,42 @@ struct SmemBF16 {
     __bf16 vt[2][D][kN + kPad];
 };
 
-template <int D>
-struct KVRegs {
-    static constexpr int KCH = kN * D / 8 / 256;                // 16-byte K chunks per thread
-    static constexpr int VUNITS = (kN / 4) * (D / 8);           // 4 keys x 8 dims units
-    static constexpr int VPT = (VUNITS + 255) / 256;            // units per thread
-    uint4 k[KCH];
-    uint4 v[VPT][4];
-};
-
-template <int D>
-__device__ inline void kv_load(const __bf16 *__restrict__ kp, const __bf16 *__restrict__ vp,
-                               size_t row0, size_t rstride, KVRegs<D> &r) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < KVRegs<D>::KCH; ++u) {
-        const int c = tid + 256 * u;
-        const int key = c / (D / 8), col = c % (D / 8);
-        r.k[u] = *reinterpret_cast<const uint4 *>(kp + row0 + key * rstride + col * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < KVRegs<D>::VPT; ++u) {
-        const int unit = tid + 256 * u;
-        if (unit < KVRegs<D>::VUNITS) {
-            const int kg = unit / (D / 8), col = unit % (D / 8);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                r.v[u][e] = *reinterpret_cast<const uint4 *>(vp + row0 + (kg * 4 + e) * rstride +
-                                                            col * 8);
-        }
-    }
-}
-
-template <int D>
-__device__ inline void kv_store(SmemBF16<D> &sm, int buf, const KVRegs<D> &r) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < KVRegs<D>::KCH; ++u) {
-        const int c = tid + 256 * u;
-        const int key = c / (D / 8), col = c % (D / 8);
-        *reinterpret_cast<uint4 *>(&sm.k[buf][key][col * 8]) = r.k[u];
-    }
-#pragma unroll
-    for (int u = 0; u < KVRegs<D>::VPT; ++u) {
-        const int unit = tid + 256 * u;
-        if (unit < KVRegs<D>::VUNITS) {
-            const int kg = unit / (D / 8), col = unit % (D / 8);
-            const uint32_t w0[4] = {r.v[u][0].x, r.v[u][0].y, r.v[u][0].z, r.v[u][0].w};
-            const uint32_t w1[4] = {r.v[u][1].x, r.v[u][1].y, r.v[u][1].z, r.v[u][1].w};
-            const uint32_t w2[4] = {r.v[u][2].x, r.v[u][2].y, r.v[u][2].z, r.v[u][2].w};
-            const uint32_t w3[4] = {r.v[u][3].x, r.v[u][3].y, r.v[u][3].z, r.v[u][3].w};
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                // dims col*8 + 2p (low halves) and col*8 + 2p + 1 (high halves), keys kg*4 .. +3
-                uint2 lo, hi;
-                lo.x = (w0[p] & 0xffffu) | (w1[p] << 16);
-                lo.y = (w2[p] & 0xffffu) | (w3[p] << 16);
-                hi.x = (w0[p] >> 16) | (w1[p] & 0xffff0000u);
-                hi.y = (w2[p] >> 16) | (w3[p] & 0xffff0000u);
-                *reinterpret_cast<uint2 *>(&sm.vt[buf][col * 8 + 2 * p][kg * 4]) = lo;
-                *reinterpret_cast<uint2 *>(&sm.vt[buf][col * 8 + 2 * p + 1][kg * 4]) = hi;
-            }
-        }
-    }
-}
-
 // K row read as A-operand row m of a 32-key S^T tile: bits 2 and 3 of m swapped.
 __device__ inline int key_of_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
+__device__ inline void unpack8(const uint4 u, float *f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(w[e] << 16);
+        f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+}
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ inline uint4 pack8(const float *f) {
+    bf16x8_t v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)f[e];
+    return __builtin_bit_cast(uint4, v);
+}
+
+__device__ inline uint2 pack4(float a, float b, float c, float d) {
+    bf16x4_t v;
+    v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
+    return __builtin_bit_cast(uint2, v);
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
-    __shared__ SmemBF16<D> sm;
+    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[sizeof(SmemBF16<D>)];
+    SmemBF16<D> &sm = *reinterpret_cast<SmemBF16<D> *>(smem_raw);
     Tile tl;
     if (!decode_tile(a, MODE, tl)) return;
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, half = lane >> 5;
     const int r = wave * 32 + col;
     const __bf16 *__restrict__ qp = static_cast<const __bf16 *>(a.q);
@@ -210,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 
     // this lane's query row
     bool rvalid;
-    int t, h, slot;
+    int t, h, slot = 0;
     if (MODE == kPast) {
         rvalid = r < tl.nrows;
         const uint64_t rec = rvalid ? a.lists[tl.row_begin + r] : 0ull;
@@ -221,7 +185,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         t = tl.t0 + r;
         rvalid = t < tl.tend;
         h = tl.h;
-        slot = tl.slot;
     }
     const int tq = rvalid ? t : 0x7fffffff;    // padding rows never mask anything
     // wave-uniform token range of the wave's rows (OWN / DENSE)
@@ -248,35 +211,92 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
     const float sl2 = a.scale_log2;
 
+    // ---- K / V staging: global -> registers -> LDS (V transposed on the way)
+    constexpr int KCH = kN * D / 8 / 256;          // 16-byte K chunks per thread
+    constexpr int VUN = (kN / 4) * (D / 8);        // units of 4 keys x 8 dims
+    static_assert(VUN <= 256, "one V unit per thread at most");
     const size_t rstride = (size_t)a.Hkv * D;
-    const size_t kvbase = ((size_t)tl.b * a.S) * rstride + (size_t)tl.g * D;
-    KVRegs<D> regs;
-    kv_load<D>(kp, vp, kvbase + (size_t)tl.key_begin * rstride, rstride, regs);
-    kv_store<D>(sm, 0, regs);
+    const __bf16 *kbase = kp + ((size_t)tl.b * a.S) * rstride + (size_t)tl.g * D;
+    const __bf16 *vbase = vp + ((size_t)tl.b * a.S) * rstride + (size_t)tl.g * D;
+    const bool vact = (VUN == 256) || tid < VUN;
+    const int vkg = tid / (D / 8), vcol = tid % (D / 8);
+    // per-thread K chunk coordinates (chunk c = tid + 256 u)
+    const int kc0 = tid, kc1 = tid + 256, kc2 = tid + 512, kc3 = tid + 768;
+    uint4 kr0, kr1, kr2, kr3, vr0, vr1, vr2, vr3;
+
+#define MOBA_KLD(c) (*reinterpret_cast<const uint4 *>(ks + ((c) / (D / 8)) * rstride + ((c) % (D / 8)) * 8))
+#define MOBA_KST(c, x) (*reinterpret_cast<uint4 *>(&sm.k[buf][(c) / (D / 8)][((c) % (D / 8)) * 8]) = (x))
+    auto load_kv = [&](int kb) {
+        const __bf16 *ks = kbase + (size_t)kb * rstride;
+        kr0 = MOBA_KLD(kc0);
+        kr1 = MOBA_KLD(kc1);
+        if constexpr (KCH > 2) {
+            kr2 = MOBA_KLD(kc2);
+            kr3 = MOBA_KLD(kc3);
+        }
+        if (vact) {
+            const __bf16 *vs = vbase + (size_t)(kb + vkg * 4) * rstride + vcol * 8;
+            vr0 = *reinterpret_cast<const uint4 *>(vs);
+            vr1 = *reinterpret_cast<const uint4 *>(vs + rstride);
+            vr2 = *reinterpret_cast<const uint4 *>(vs + 2 * rstride);
+            vr3 = *reinterpret_cast<const uint4 *>(vs + 3 * rstride);
+        }
+    };
+    auto store_kv = [&](int buf) {
+        MOBA_KST(kc0, kr0);
+        MOBA_KST(kc1, kr1);
+        if constexpr (KCH > 2) {
+            MOBA_KST(kc2, kr2);
+            MOBA_KST(kc3, kr3);
+        }
+        if (vact) {
+            // dims vcol*8 + 2p (low halves) and + 2p + 1 (high halves), keys vkg*4 .. +3
+            __bf16 *dst = &sm.vt[buf][vcol * 8][vkg * 4];
+            constexpr int VS = kN + kPad;
+#define MOBA_VT(p, a0, a1, a2, a3)                                                        \
+            {                                                                             \
+                uint2 lo, hi;                                                             \
+                lo.x = ((a0) & 0xffffu) | ((a1) << 16);                                   \
+                lo.y = ((a2) & 0xffffu) | ((a3) << 16);                                   \
+                hi.x = ((a0) >> 16) | ((a1) & 0xffff0000u);                               \
+                hi.y = ((a2) >> 16) | ((a3) & 0xffff0000u);                               \
+                *reinterpret_cast<uint2 *>(dst + (2 * (p)) * VS) = lo;                    \
+                *reinterpret_cast<uint2 *>(dst + (2 * (p) + 1) * VS) = hi;                \
+            }
+            MOBA_VT(0, vr0.x, vr1.x, vr2.x, vr3.x)
+            MOBA_VT(1, vr0.y, vr1.y, vr2.y, vr3.y)
+            MOBA_VT(2, vr0.z, vr1.z, vr2.z, vr3.z)
+            MOBA_VT(3, vr0.w, vr1.w, vr2.w, vr3.w)
+#undef MOBA_VT
+        }
+    };
+#undef MOBA_KLD
+#undef MOBA_KST
+
+    load_kv(tl.key_begin);
+    store_kv(0);
     __syncthreads();
 
     const int krow = key_of_row(col);
+    const f32x16_t zero16 = {};
     for (int s = 0; s < tl.nsub; ++s) {
         const int buf = s & 1;
         const int kb = tl.key_begin + s * kN;
-        const bool more = s + 1 < tl.nsub;
-        if (more) kv_load<D>(kp, vp, kvbase + (size_t)(kb + kN) * rstride, rstride, regs);
+        // prefetch the next sub-tile (the last iteration re-reads the last one)
+        load_kv(tl.key_begin + min(s + 1, tl.nsub - 1) * kN);
 
         if (MODE == kPast || kb <= wtmax) {
-            // S^T tiles: rows = keys, columns = this wave's 32 queries
             f32x16_t sacc[kN / 32];
 #pragma unroll
             for (int kt = 0; kt < kN / 32; ++kt) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
-#pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) {
                     const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(
                         &sm.k[buf][kt * 32 + krow][kk * 16 + half * 8]);
-                    sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[kk], sacc[kt], 0, 0, 0);
+                    sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        av, qf[kk], kk == 0 ? zero16 : sacc[kt], 0, 0, 0);
                 }
             }
-            // causal mask on sub-tiles that cross the diagonal
             if (MODE != kPast && kb + kN - 1 > wtmin) {
 #pragma unroll
                 for (int kt = 0; kt < kN / 32; ++kt)
@@ -290,27 +310,29 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int kt = 0; kt < kN / 32; ++kt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run, mx * sl2);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            m_run = m_new;
+                for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kt][i], sacc[kt][i + 1]));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+            if (__any(mx > m_run + kRescaleSlack)) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+            }
             float psum = 0.f;
             bf16x8_t pb[kN / 32][2];
 #pragma unroll
             for (int kt = 0; kt < kN / 32; ++kt)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], sl2, -m_use));
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], sl2, -m_run));
                     psum += pv;
                     pb[kt][i >> 3][i & 7] = (__bf16)pv;
                 }
-            l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+            l_run += psum;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -322,31 +344,93 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt][h2], oacc[dt], 0, 0, 0);
                     }
         }
-        if (more) kv_store<D>(sm, buf ^ 1, regs);
+        if (s + 1 < tl.nsub) store_kv(buf ^ 1);
         __syncthreads();
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    if (!rvalid) return;
     const float inv = 1.f / l_tot;
-    __bf16 *dst;
-    if (MODE == kDense) {
-        dst = static_cast<__bf16 *>(a.out) + (((size_t)tl.b * a.S + t) * a.Hq + h) * D;
-    } else {
-        const size_t row_id = ((size_t)tl.b * a.Hq + h) * a.S + t;
-        dst = static_cast<__bf16 *>(a.part_o) + (row_id * a.topk + slot) * D;
-        if (half == 0) a.part_lse[row_id * a.topk + slot] = m_run + __log2f(l_tot);
+    const float lse = m_run + __log2f(l_tot);
+    constexpr int LPR = D / 8;          // lanes per 256-byte (D = 128) output row
+    constexpr int RPP = 64 / LPR;       // rows per store pass
+
+    if (MODE == kPast) {
+        // normalised partial (bf16) -> LDS -> whole-row stores
+        __bf16 *stg = reinterpret_cast<__bf16 *>(smem_raw) + wave * 32 * (D + kPad);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                *reinterpret_cast<uint2 *>(stg + col * (D + kPad) + dt * 32 + 8 * g4 + 4 * half) =
+                    pack4(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv,
+                          oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
+            }
+        const long long row_slot_id =
+            rvalid ? (((long long)tl.b * a.Hq + h) * a.S + t) * a.nslot + slot : -1ll;
+        if (rvalid && half == 0) a.part_lse[row_slot_id] = lse;
+        __syncthreads();
+        __bf16 *po = static_cast<__bf16 *>(a.part_o);
+        const int lo32 = (int)(row_slot_id & 0xffffffffll), hi32 = (int)(row_slot_id >> 32);
+#pragma unroll
+        for (int it = 0; it < 32 / RPP; ++it) {
+            const int rr = it * RPP + lane / LPR, ch = lane % LPR;
+            const long long id = ((long long)__shfl(hi32, rr, 64) << 32) |
+                                 (unsigned)__shfl(lo32, rr, 64);
+            if (id >= 0)
+                *reinterpret_cast<uint4 *>(po + id * D + ch * 8) =
+                    *reinterpret_cast<const uint4 *>(stg + rr * (D + kPad) + ch * 8);
+        }
+        return;
     }
+
+    // OWN / DENSE: own result (fp32) -> LDS, then merge with the past partials
+    float *stf = reinterpret_cast<float *>(smem_raw) + wave * 32 * (D + 4);
+    float *stl = reinterpret_cast<float *>(smem_raw) + 4 * 32 * (D + 4) + wave * 32;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const int d0 = dt * 32 + 8 * g4 + 4 * half;
-            union { __bf16 hv[4]; uint2 u; } pk;
+        for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<float4 *>(stf + col * (D + 4) + dt * 32 + 8 * g4 + 4 * half) =
+                make_float4(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv,
+                            oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
+    if (half == 0) stl[col] = lse;
+    __syncthreads();
+    const __bf16 *po = static_cast<const __bf16 *>(a.part_o);
+    __bf16 *outp = static_cast<__bf16 *>(a.out);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pk.hv[e] = (__bf16)(oacc[dt][4 * g4 + e] * inv);
-            *reinterpret_cast<uint2 *>(dst + d0) = pk.u;
+    for (int it = 0; it < 32 / RPP; ++it) {
+        const int rr = it * RPP + lane / LPR, ch = lane % LPR;
+        const int tr = tl.t0 + wave * 32 + rr;
+        if (tr >= tl.tend) continue;
+        float o[8];
+        const float4 x0 = *reinterpret_cast<const float4 *>(stf + rr * (D + 4) + ch * 8);
+        const float4 x1 = *reinterpret_cast<const float4 *>(stf + rr * (D + 4) + ch * 8 + 4);
+        o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
+        o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
+        if (MODE == kOwn && tl.npast > 0) {
+            const long long rid = (((long long)tl.b * a.Hq + tl.h) * a.S + tr) * a.nslot;
+            const float lo = stl[rr];
+            float mxl = lo;
+            for (int sl = 0; sl < tl.npast; ++sl) mxl = fmaxf(mxl, a.part_lse[rid + sl]);
+            const float wo = exp2f(lo - mxl);
+            float wsum = wo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= wo;
+            for (int sl = 0; sl < tl.npast; ++sl) {
+                const float w = exp2f(a.part_lse[rid + sl] - mxl);
+                wsum += w;
+                float f[8];
+                unpack8(*reinterpret_cast<const uint4 *>(po + (rid + sl) * D + ch * 8), f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = fmaf(w, f[e], o[e]);
+            }
+            const float iw = 1.f / wsum;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= iw;
         }
+        *reinterpret_cast<uint4 *>(outp + (((size_t)tl.b * a.S + tr) * a.Hq + tl.h) * D + ch * 8) =
+            pack8(o);
+    }
 }
 
 // ------------------------------------------------------------------ fp32 VALU path
@@ -354,7 +438,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 // fp32 inputs keep fp32 end to end (no matrix-core rounding).  Two threads
 // share a query row, each holding half of the head dimensions; the partial
 // dot products meet through one lane exchange.  Keys stream through LDS in
-// sub-tiles of 32.
+// sub-tiles of 32.  The own-block pass merges the past partials of its row.
 
 constexpr int kNF = 32;
 
@@ -371,7 +455,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const float *__restrict__ vp = static_cast<const float *>(a.v);
 
     bool rvalid;
-    int t, h, slot;
+    int t, h, slot = 0;
     if (MODE == kPast) {
         rvalid = r < tl.nrows;
         const uint64_t rec = rvalid ? a.lists[tl.row_begin + r] : 0ull;
@@ -382,7 +466,6 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
         t = tl.t0 + r;
         rvalid = t < tl.tend;
         h = tl.h;
-        slot = tl.slot;
     }
     const int tq = rvalid ? t : 0x7fffffff;
     float qv[DH], o[DH];
@@ -434,80 +517,38 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     }
     if (!rvalid) return;
     const float inv = 1.f / l_run;
-    float *dst;
-    if (MODE == kDense) {
-        dst = static_cast<float *>(a.out) + (((size_t)tl.b * a.S + t) * a.Hq + h) * D;
-    } else {
-        const size_t row_id = ((size_t)tl.b * a.Hq + h) * a.S + t;
-        dst = static_cast<float *>(a.part_o) + (row_id * a.topk + slot) * D;
-        if (dh == 0) a.part_lse[row_id * a.topk + slot] = m_run + log2f(l_run);
+    const float lse = m_run + log2f(l_run);
+    const long long row_id = ((long long)tl.b * a.Hq + h) * a.S + t;
+    if (MODE == kPast) {
+        float *dst = static_cast<float *>(a.part_o) + (row_id * a.nslot + slot) * D + dh * DH;
+#pragma unroll
+        for (int i = 0; i < DH; ++i) dst[i] = o[i] * inv;
+        if (dh == 0) a.part_lse[row_id * a.nslot + slot] = lse;
+        return;
     }
 #pragma unroll
-    for (int i = 0; i < DH; ++i) dst[dh * DH + i] = o[i] * inv;
-}
-
-// ------------------------------------------------------------------ merge
-//
-// out = sum_s w_s O_s / sum_s w_s with w_s = 2^(lse_s - max lse): the exact
-// combination of softmaxes over disjoint key sets.  D/8 threads per row, 8
-// dimensions each.
-
-__device__ inline void ld8(const __bf16 *p, float *f) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int i = 0; i < DH; ++i) o[i] *= inv;
+    if (MODE == kOwn && tl.npast > 0) {
+        const float *ls = a.part_lse + row_id * a.nslot;
+        float mxl = lse;
+        for (int sl = 0; sl < tl.npast; ++sl) mxl = fmaxf(mxl, ls[sl]);
+        const float wo = exp2f(lse - mxl);
+        float wsum = wo;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        f[2 * e] = __uint_as_float(w[e] << 16);
-        f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        for (int i = 0; i < DH; ++i) o[i] *= wo;
+        for (int sl = 0; sl < tl.npast; ++sl) {
+            const float w = exp2f(ls[sl] - mxl);
+            wsum += w;
+            const float *src = static_cast<const float *>(a.part_o) + (row_id * a.nslot + sl) * D + dh * DH;
+#pragma unroll
+            for (int i = 0; i < DH; ++i) o[i] = fmaf(w, src[i], o[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < DH; ++i) o[i] /= wsum;
     }
-}
-__device__ inline void ld8(const float *p, float *f) {
-    const float4 x = *reinterpret_cast<const float4 *>(p);
-    const float4 y = *reinterpret_cast<const float4 *>(p + 4);
-    f[0] = x.x; f[1] = x.y; f[2] = x.z; f[3] = x.w;
-    f[4] = y.x; f[5] = y.y; f[6] = y.z; f[7] = y.w;
-}
-__device__ inline void st8(__bf16 *p, const float *f) {
-    union { __bf16 h[8]; uint4 u; } pk;
+    float *dst = static_cast<float *>(a.out) + (((size_t)tl.b * a.S + t) * a.Hq + h) * D + dh * DH;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pk.h[e] = (__bf16)f[e];
-    *reinterpret_cast<uint4 *>(p) = pk.u;
-}
-__device__ inline void st8(float *p, const float *f) {
-    *reinterpret_cast<float4 *>(p) = make_float4(f[0], f[1], f[2], f[3]);
-    *reinterpret_cast<float4 *>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, long long rows) {
-    constexpr int TPR = D / 8;
-    constexpr int RPW = 256 / TPR;
-    const long long row_id = (long long)blockIdx.x * RPW + threadIdx.x / TPR;
-    if (row_id >= rows) return;
-    const int d0 = (threadIdx.x % TPR) * 8;
-    const int t = (int)(row_id % a.S);
-    const long long bh = row_id / a.S;
-    const int h = (int)(bh % a.Hq);
-    const int b = (int)(bh / a.Hq);
-    const int nsel = min(a.topk, t / a.B + 1);
-    const float *ls = a.part_lse + row_id * a.topk;
-    float mx = -INFINITY;
-    for (int s = 0; s < nsel; ++s) mx = fmaxf(mx, ls[s]);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    const T *po = static_cast<const T *>(a.part_o) + (size_t)row_id * a.topk * D + d0;
-    for (int s = 0; s < nsel; ++s) {
-        const float w = exp2f(ls[s] - mx);
-        wsum += w;
-        float f[8];
-        ld8(po + (size_t)s * D, f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, f[e], acc[e]);
-    }
-    const float inv = 1.f / wsum;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= inv;
-    st8(static_cast<T *>(a.out) + (((size_t)b * a.S + t) * a.Hq + h) * D + d0, acc);
+    for (int i = 0; i < DH; ++i) dst[i] = o[i];
 }
 
 // ------------------------------------------------------------------ launchers
@@ -519,6 +560,7 @@ static AttnArgs make_args(const AttnBuffers &bf, const Problem &p) {
     a.lists = bf.lists; a.list_off = bf.list_off; a.tile_off = bf.tile_off;
     a.batch = p.batch; a.S = p.S; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.B = p.B; a.n = p.n;
     a.topk = p.topk;
+    a.nslot = part_slots(p);
     a.L = (long long)p.batch * p.Hkv * p.n;
     a.ntiles = 0;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.D));
@@ -558,21 +600,6 @@ hipError_t launch_attn_dense(const AttnBuffers &bf, const Problem &p, hipStream_
     const unsigned long long ntt = (p.S + kTileRows - 1) / kTileRows;
     a.ntiles = (unsigned)(ntt * p.batch * p.Hq);
     return attn_launch<kDense>(a, p, round8(a.ntiles), st);
-}
-
-hipError_t launch_merge(const AttnBuffers &bf, const Problem &p, hipStream_t st) {
-    AttnArgs a = make_args(bf, p);
-    const long long rows = (long long)p.batch * p.Hq * p.S;
-    const int rpw = 256 / (p.D / 8);
-    const unsigned grid = (unsigned)((rows + rpw - 1) / rpw);
-    if (p.dtype == kBF16) {
-        if (p.D == 64) merge_kernel<__bf16, 64><<<grid, 256, 0, st>>>(a, rows);
-        else merge_kernel<__bf16, 128><<<grid, 256, 0, st>>>(a, rows);
-    } else {
-        if (p.D == 64) merge_kernel<float, 64><<<grid, 256, 0, st>>>(a, rows);
-        else merge_kernel<float, 128><<<grid, 256, 0, st>>>(a, rows);
-    }
-    return hipGetLastError();
 }
 
 }  // namespace moba

@@ -70,8 +70,8 @@ Layout prefill_layout(const Problem &p) {
     l.list_off = off; off += align_up((L + 1) * 8);
     l.tile_off = off; off += align_up((L + 1) * 4);
     l.lists = off; off += align_up((size_t)past_rows(p) * 8);
-    l.part_o = off; off += align_up(rows * p.topk * p.D * elem_size(p));
-    l.part_lse = off; off += align_up(rows * p.topk * 4);
+    l.part_o = off; off += align_up(rows * part_slots(p) * p.D * elem_size(p));
+    l.part_lse = off; off += align_up(rows * part_slots(p) * 4);
     l.total = off;
     return l;
 }
@@ -155,8 +155,6 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
         return MOBA_ERR_HIP;
     if ((e = E.mark(MOBA_STAGE_ATTN_OWN)) != hipSuccess) return MOBA_ERR_HIP;
     if ((e = launch_attn_own(bf, p, st)) != hipSuccess) return MOBA_ERR_HIP;
-    if ((e = E.mark(MOBA_STAGE_MERGE)) != hipSuccess) return MOBA_ERR_HIP;
-    if ((e = launch_merge(bf, p, st)) != hipSuccess) return MOBA_ERR_HIP;
     if ((e = E.mark(MOBA_NUM_STAGES)) != hipSuccess) return MOBA_ERR_HIP;
     return MOBA_OK;
 }

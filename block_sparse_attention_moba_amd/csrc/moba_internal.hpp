@@ -51,8 +51,8 @@ hipError_t launch_index(const int32_t *idx, uint32_t *cnt, uint32_t *cursor, uin
 struct AttnBuffers {
     const void *q, *k, *v;
     void *out;
-    void *part_o;           // [row][topk][D], dtype-sized elements
-    float *part_lse;        // [row][topk], base-2 log-sum-exp of the scaled logits
+    void *part_o;           // [row][slots][D], dtype-sized elements
+    float *part_lse;        // [row][slots], base-2 log-sum-exp of the scaled logits
     const uint64_t *lists;
     const uint64_t *list_off;
     const uint32_t *tile_off;
@@ -61,7 +61,9 @@ hipError_t launch_attn_past(const AttnBuffers &b, const Problem &p, uint64_t til
                             hipStream_t st);
 hipError_t launch_attn_own(const AttnBuffers &b, const Problem &p, hipStream_t st);
 hipError_t launch_attn_dense(const AttnBuffers &b, const Problem &p, hipStream_t st);
-hipError_t launch_merge(const AttnBuffers &b, const Problem &p, hipStream_t st);
+
+// Partial-output slots per query row: one per selectable past block.
+inline int part_slots(const Problem &p) { return p.topk > 1 ? p.topk - 1 : 1; }
 
 // Pool partial-sum chunk length (tokens) for a block size that is a multiple of 64.
 inline int pool_chunk(int B) { return (B % 256 == 0) ? 256 : (B % 128 == 0 ? 128 : 64); }

@@ -80,9 +80,10 @@ enum {
     MOBA_STAGE_GATE = 1,     /* gate scores + causal top-k                        */
     MOBA_STAGE_INDEX = 2,    /* per-(KV head, block) lists of the query rows      */
     MOBA_STAGE_ATTN_PAST = 3,/* attention of listed rows over one past block each */
-    MOBA_STAGE_ATTN_OWN = 4, /* causal attention over each query's own block      */
-    MOBA_STAGE_MERGE = 5,    /* online-softmax merge of the partial outputs       */
-    MOBA_NUM_STAGES = 6
+    MOBA_STAGE_ATTN_OWN = 4, /* causal attention over each query's own block,
+                                fused with the online-softmax merge of the
+                                partial outputs                                   */
+    MOBA_NUM_STAGES = 5
 };
 
 /* ABI version of the loaded library (MOBA_ABI_VERSION at build time). */
@@ -139,7 +140,8 @@ moba_status_t moba_prefill(const void *q, const void *k, const void *v, void *ou
  * moba_prefill that also records caller-created hipEvent_t handles on
  * `stream`: stage_events[s] just before stage s (MOBA_STAGE_*) and
  * stage_events[MOBA_NUM_STAGES] after the last stage; stages that a problem
- * does not need record back-to-back events.  stage_events must hold
+ * does not need record back-to-back events.  With topk >= seqlen /
+ * block_size the full causal attention is timed as MOBA_STAGE_ATTN_PAST.  stage_events must hold
  * MOBA_NUM_STAGES + 1 valid events.
  */
 moba_status_t moba_prefill_timed(const void *q, const void *k, const void *v, void *out,
