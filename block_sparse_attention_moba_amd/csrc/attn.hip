@@ -22,11 +22,11 @@
 // 64, double-buffered through registers.  S^T = K Q^T and O^T += V^T P^T run
 // on v_mfma_f32_32x32x16_bf16 with fp32 accumulation: a lane holds one query
 // column and 16 keys of each 32-key S^T tile, so the softmax row reductions
-// are in-lane plus one exchange with lane ^ 32.  The A-operand rows of S^T are
-// read from K rows whose index has bits 2 and 3 swapped, which makes the 8
-// P values each lane feeds to the PV product 8 consecutive keys; V is stored
-// transposed in LDS (register transpose on the way in) so that the V^T
-// operand is one 16-byte LDS read.  The running maximum is only moved (and O
+// are in-lane plus one exchange with lane ^ 32.  V is stored transposed in
+// LDS (register transpose on the way in) with the key columns of every
+// 16-key group in bit-2/bit-3-swapped order: the 8 P values a lane feeds to
+// the PV product then sit at 8 consecutive columns, so the V^T operand is one
+// 16-byte LDS read, and the K operand rows stay in natural order.  The running maximum is only moved (and O
 // rescaled) when a row's new maximum exceeds it by more than 2^8, which
 // keeps every exponent <= 2^8 and skips almost all rescales.  Results leave
 // through LDS so that every global store writes whole 16-byte pieces of
@@ -130,8 +130,8 @@ struct SmemBF16 {
     __bf16 vt[2][D][kN + kPad];
 };
 
-// K row read as A-operand row m of a 32-key S^T tile: bits 2 and 3 of m swapped.
-__device__ inline int key_of_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+// LDS column of key k in the transposed V tile: bits 2 and 3 of k swapped.
+__host__ __device__ constexpr int vt_col(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 __device__ inline void unpack8(const uint4 u, float *f) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -219,7 +219,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const __bf16 *kbase = kp + ((size_t)tl.b * a.S) * rstride + (size_t)tl.g * D;
     const __bf16 *vbase = vp + ((size_t)tl.b * a.S) * rstride + (size_t)tl.g * D;
     const bool vact = (VUN == 256) || tid < VUN;
-    const int vkg = tid / (D / 8), vcol = tid % (D / 8);
+    // V units: consecutive lanes take consecutive 4-key groups, so one LDS store
+    // instruction of 16 lanes fills a whole 128-byte row of the transposed tile
+    const int vkg = tid % (kN / 4), vcol = tid / (kN / 4);
     // per-thread K chunk coordinates (chunk c = tid + 256 u)
     const int kc0 = tid, kc1 = tid + 256, kc2 = tid + 512, kc3 = tid + 768;
     uint4 kr0, kr1, kr2, kr3, vr0, vr1, vr2, vr3;
@@ -251,15 +253,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         }
         if (vact) {
             // dims vcol*8 + 2p (low halves) and + 2p + 1 (high halves), keys vkg*4 .. +3
-            __bf16 *dst = &sm.vt[buf][vcol * 8][vkg * 4];
+            __bf16 *dst = &sm.vt[buf][vcol * 8][vt_col(vkg * 4)];
             constexpr int VS = kN + kPad;
+            constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;   // v_perm byte selectors
 #define MOBA_VT(p, a0, a1, a2, a3)                                                        \
             {                                                                             \
                 uint2 lo, hi;                                                             \
-                lo.x = ((a0) & 0xffffu) | ((a1) << 16);                                   \
-                lo.y = ((a2) & 0xffffu) | ((a3) << 16);                                   \
-                hi.x = ((a0) >> 16) | ((a1) & 0xffff0000u);                               \
-                hi.y = ((a2) >> 16) | ((a3) & 0xffff0000u);                               \
+                lo.x = __builtin_amdgcn_perm((a1), (a0), kLo);                            \
+                lo.y = __builtin_amdgcn_perm((a3), (a2), kLo);                            \
+                hi.x = __builtin_amdgcn_perm((a1), (a0), kHi);                            \
+                hi.y = __builtin_amdgcn_perm((a3), (a2), kHi);                            \
                 *reinterpret_cast<uint2 *>(dst + (2 * (p)) * VS) = lo;                    \
                 *reinterpret_cast<uint2 *>(dst + (2 * (p) + 1) * VS) = hi;                \
             }
@@ -277,7 +280,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     store_kv(0);
     __syncthreads();
 
-    const int krow = key_of_row(col);
     const f32x16_t zero16 = {};
     for (int s = 0; s < tl.nsub; ++s) {
         const int buf = s & 1;
@@ -292,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
                 for (int kk = 0; kk < D / 16; ++kk) {
                     const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(
-                        &sm.k[buf][kt * 32 + krow][kk * 16 + half * 8]);
+                        &sm.k[buf][kt * 32 + col][kk * 16 + half * 8]);
                     sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         av, qf[kk], kk == 0 ? zero16 : sacc[kt], 0, 0, 0);
                 }
@@ -302,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                 for (int kt = 0; kt < kN / 32; ++kt)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int key = kb + kt * 32 + 16 * (i >> 3) + 8 * half + 4 * ((i >> 2) & 1) + (i & 3);
+                        const int key = kb + kt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
                         if (key > tq) sacc[kt][i] = -INFINITY;
                     }
             }
