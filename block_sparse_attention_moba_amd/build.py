@@ -27,8 +27,10 @@ FLAGS = [
 ]
 # The attention kernels never see NaN inputs on their own arithmetic paths
 # (masked logits are -inf, not NaN): without IEEE mode, fmaxf needs no
-# quieting of its operands.
-EXTRA = {"attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# quieting of its operands.  Matrix-core results go to ordinary vector
+# registers, so the softmax reads the logits without copies out of the
+# accumulation registers.
+EXTRA = {"attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():

@@ -7,31 +7,23 @@
 // "技術細節與優勢": the own block is always attended, causally).
 //
 // Three tile kinds share one kernel body:
-//   PAST  : up to 128 listed query rows of one (batch, KV head, past block j)
+//   PAST  : up to M listed query rows of one (batch, KV head, past block j)
 //           attend all B keys of block j (fully visible, no mask) and write a
 //           normalised partial output plus its base-2 log-sum-exp to the
 //           row's slot of the partial buffer;
-//   OWN   : 128 consecutive query rows of one head attend their own block
+//   OWN   : M consecutive query rows of one head attend their own block
 //           causally (mask only on the sub-tiles that cross the diagonal),
 //           then merge with the row's past-block partials and write the
 //           final output;
-//   DENSE : 128 consecutive query rows attend every key <= t and write the
+//   DENSE : M consecutive query rows attend every key <= t and write the
 //           final output (full causal attention, used when every causal block
 //           is selected).
-// Four waves each own 32 query rows.  Keys stream through LDS in sub-tiles of
-// 64, double-buffered through registers.  S^T = K Q^T and O^T += V^T P^T run
-// on v_mfma_f32_32x32x16_bf16 with fp32 accumulation: a lane holds one query
-// column and 16 keys of each 32-key S^T tile, so the softmax row reductions
-// are in-lane plus one exchange with lane ^ 32.  V is stored transposed in
-// LDS (register transpose on the way in) with the key columns of every
-// 16-key group in bit-2/bit-3-swapped order: the 8 P values a lane feeds to
-// the PV product then sit at 8 consecutive columns, so the V^T operand is one
-// 16-byte LDS read, and the K operand rows stay in natural order.  The running maximum is only moved (and O
-// rescaled) when a row's new maximum exceeds it by more than 2^8, which
-// keeps every exponent <= 2^8 and skips almost all rescales.  Results leave
-// through LDS so that every global store writes whole 16-byte pieces of
-// contiguous 256-byte rows.
+// M is 256 for bf16 (matrix-core path below) and 128 for fp32 (vector path).
+// Results leave through LDS so that every global store writes whole 16-byte
+// pieces of contiguous rows.
 #include <math.h>
+
+#include <type_traits>
 
 #include "moba_internal.hpp"
 
@@ -39,8 +31,6 @@ namespace moba {
 
 enum Mode { kPast = 0, kOwn = 1, kDense = 2 };
 
-constexpr int kN = 64;                // keys per sub-tile
-constexpr int kPad = 8;               // LDS row padding (elements) against bank conflicts
 constexpr float kRescaleSlack = 8.f;  // log2 units a row max may exceed the running max
 
 struct AttnArgs {
@@ -50,16 +40,20 @@ struct AttnArgs {
     float *part_lse;
     const uint64_t *lists, *list_off;
     const uint32_t *tile_off;
+    const float *kmax2;    // [batch][Hkv][n] largest squared key norm per block
     int batch, S, Hq, Hkv, G, B, n, topk, nslot;
+    int M;                 // query rows per tile
     long long L;           // number of lists
     unsigned ntiles;       // tiles of OWN / DENSE launches
     float scale_log2;      // log2(e) / sqrt(D)
+    unsigned *defer_count;  // tiles whose logit bound fails, for the tracking pass
+    unsigned *defer_list;
 };
 
 struct Tile {
     int b, g;
     int key_begin;   // first key of the range
-    int nsub;        // sub-tiles of kN keys to visit
+    int nslice;      // slices of 32 keys to visit (bf16 path)
     int tmax;        // last token of the tile's rows (OWN / DENSE)
     // PAST
     uint64_t row_begin;
@@ -68,8 +62,7 @@ struct Tile {
     int t0, h, tend, npast;
 };
 
-__device__ inline bool decode_tile(const AttnArgs &a, int mode, Tile &tl) {
-    const unsigned tile = xcd_tile(blockIdx.x, gridDim.x);
+__device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, Tile &tl) {
     if (mode == kPast) {
         const long long L = a.L;
         if (tile >= a.tile_off[L]) return false;
@@ -83,17 +76,17 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, Tile &tl) {
         const int j = (int)(lid % a.n);
         tl.g = (int)((lid / a.n) % a.Hkv);
         tl.b = (int)(lid / ((long long)a.n * a.Hkv));
-        tl.row_begin = a.list_off[lid] + (uint64_t)(tile - a.tile_off[lid]) * kTileRows;
+        tl.row_begin = a.list_off[lid] + (uint64_t)(tile - a.tile_off[lid]) * a.M;
         const uint64_t rend = a.list_off[lid + 1];
-        tl.nrows = (int)min((uint64_t)kTileRows, rend - tl.row_begin);
+        tl.nrows = (int)min((uint64_t)a.M, rend - tl.row_begin);
         tl.key_begin = j * a.B;
-        tl.nsub = a.B / kN;
+        tl.nslice = a.B / 32;
         tl.tmax = 0x7fffffff;
         return true;
     }
     if (tile >= a.ntiles) return false;
     if (mode == kOwn) {
-        const int tpb = (a.B + kTileRows - 1) / kTileRows;
+        const int tpb = (a.B + a.M - 1) / a.M;
         unsigned rest = tile;
         const int tt = rest % tpb; rest /= tpb;
         const int hh = rest % a.G; rest /= a.G;
@@ -101,37 +94,78 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, Tile &tl) {
         tl.g = rest % a.Hkv;
         tl.b = rest / a.Hkv;
         tl.h = tl.g * a.G + hh;
-        tl.t0 = i * a.B + tt * kTileRows;
+        tl.t0 = i * a.B + tt * a.M;
         tl.tend = i * a.B + a.B;
         tl.key_begin = i * a.B;
         tl.npast = min(a.topk - 1, i);
     } else {
-        const int ntt = (a.S + kTileRows - 1) / kTileRows;
+        const int ntt = (a.S + a.M - 1) / a.M;
         const int bh = tile % (a.batch * a.Hq);
         const int tt = ntt - 1 - (int)(tile / (a.batch * a.Hq));
         tl.b = bh / a.Hq;
         tl.h = bh % a.Hq;
         tl.g = tl.h / a.G;
-        tl.t0 = tt * kTileRows;
+        tl.t0 = tt * a.M;
         tl.tend = a.S;
         tl.key_begin = 0;
         tl.npast = 0;
     }
-    tl.tmax = min(tl.t0 + kTileRows, tl.tend) - 1;
-    tl.nsub = (tl.tmax - tl.key_begin) / kN + 1;
+    tl.tmax = min(tl.t0 + a.M, tl.tend) - 1;
+    tl.nslice = (tl.tmax - tl.key_begin) / 32 + 1;
     return true;
 }
 
 // ------------------------------------------------------------------ bf16 MFMA path
+//
+// One workgroup = 4 waves = 256 query rows.  Each wave owns 64 rows as two
+// 32-query column groups, so every K or V^T operand read from LDS feeds two
+// MFMAs.  One wave per SIMD (512 registers), so O stays in accumulation
+// registers.  Keys are consumed in slices of 32.  Step h pairs the matrix-core
+// work of one slice with the vector work of the previous one:
+//   S(h+1) = K(h+1) Q^T    (matrix cores)
+//   P(h) = 2^(S(h) - m), row sums, O += V(h)^T P(h)^T
+//   mask and row max of S(h+1), so that step h+1 knows whether its running
+//   maximum has to move before it exponentiates.
+//
+// K and V travel from global memory straight into LDS (global_load_lds, 16
+// bytes per lane, no registers) as row-major [key][d] slices whose 16-byte
+// chunks are XOR-swizzled per row.  Both rings have 4 slots: step h reads
+// K(h+1) and V(h) while K(h+3) and V(h+2) are in flight, so every load has two
+// steps to land.  The compiler must see that no read aliases a load in
+// flight, or it waits for the load before the read, so every slot is its own
+// LDS array and the loop is unrolled by 4 with the slots named at each step.
+// K operand rows are single 16-byte reads (swizzle: row mod 16).  The V^T
+// operand of the PV product is assembled by two transposing reads
+// (ds_read_b64_tr_b16): within each 16-lane group, lane j receives element
+// j mod 4 of the 8 bytes that lane 4e + j/4 addresses, for e = 0..3, so 16
+// lanes addressing 4 key rows x 4 dim chunks each receive 4 keys of one dim.
+// The V swizzle (chunk ^ {0, 4, 10, 14}[row mod 4]) keeps both 16-lane and
+// 32-lane servicing of those reads conflict-free.
+//
+// The MFMA yields raw q.k in fp32; the softmax scale log2(e)/sqrt(d) is
+// applied in fp32 at the exponent, so logits are in log2 units there.  Every
+// logit of a tile is bounded by |q| * max|k| (Cauchy-Schwarz, max|k| per
+// block from the pool pass).  When that bound, in log2 units, is <= 64 for
+// every row of the tile, 2^s can neither overflow nor underflow, so the
+// softmax runs against a fixed reference of 0: no row max, no rescale, no
+// subtraction.  Otherwise the tile goes to the tracking pass, which keeps a
+// running max (moved lazily, only when a row max exceeds it by more than 2^8).
 
+constexpr int kWaveRows = 64;
+constexpr int kS = 32;                 // keys per slice
+
+// 16-byte chunk swizzles (XOR on the chunk index within a row)
 template <int D>
-struct SmemBF16 {
-    __bf16 k[2][kN][D + kPad];
-    __bf16 vt[2][D][kN + kPad];
-};
+__device__ inline int swz_k(int r) { return r & (D / 8 - 1); }
+template <int D>
+__device__ inline int swz_v(int r) {
+    if constexpr (D == 128) return (0xEA40 >> (4 * (r & 3))) & 15;   // {0, 4, 10, 14}
+    else return 2 * (r & 3);
+}
 
-// LDS column of key k in the transposed V tile: bits 2 and 3 of k swapped.
-__host__ __device__ constexpr int vt_col(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ inline void unpack8(const uint4 u, float *f) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -141,8 +175,6 @@ __device__ inline void unpack8(const uint4 u, float *f) {
         f[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
     }
 }
-
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ inline uint4 pack8(const float *f) {
     bf16x8_t v;
@@ -157,283 +189,522 @@ __device__ inline uint2 pack4(float a, float b, float c, float d) {
     return __builtin_bit_cast(uint2, v);
 }
 
-template <int D, int MODE>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[sizeof(SmemBF16<D>)];
-    SmemBF16<D> &sm = *reinterpret_cast<SmemBF16<D> *>(smem_raw);
+// End of a pipeline step: this wave's loads other than the newest n have
+// landed and its LDS reads have completed (vmcnt <= n, lgkmcnt = 0), then the
+// workgroup meets.  A plain s_barrier: the workgroup fence of __syncthreads
+// would also wait for the newest loads.  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+template <int n>
+__device__ __forceinline__ void ring_barrier() {
+    static_assert(n < 16, "vmcnt immediate");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(n | 0x70);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Instruction interleave of the two phases of a pipeline step (scheduler
+// groups: 0x008 matrix-core ops, 0x100 LDS reads, 0x010 global memory,
+// 0x402 vector ALU incl. transcendental).  Phase A: each S MFMA with one V^T
+// read and a share of the exponentials.  Phase B: the K operand reads first,
+// then each PV MFMA with the staging loads and the rest of the exponentials.
+#define MOBA_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+template <int D>
+__device__ __forceinline__ void sched_phase_a_t() {
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) {
+        MOBA_SCHED(0x008, 1);
+        MOBA_SCHED(0x100, 1);
+        MOBA_SCHED(0x002, 3);
+    }
+}
+template <int D, int NLOAD>
+__device__ __forceinline__ void sched_phase_b_t() {
+    MOBA_SCHED(0x100, D / 16);             // K operand reads first
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {     // PV of group 0 || P of group 1, loads
+        MOBA_SCHED(0x008, 1);
+        if (i < NLOAD) MOBA_SCHED(0x010, 1);
+        MOBA_SCHED(0x002, 4);
+    }
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) {     // PV of group 1
+        MOBA_SCHED(0x008, 1);
+        MOBA_SCHED(0x002, 2);
+    }
+}
+
+// One tile.  FAST: the bounded softmax; a tile whose bound fails is appended
+// to the deferred list and left to the tracking pass.  !FAST: running-max
+// tracking.  PAD (PAST only): the block's slice count is not a multiple of 4,
+// so the loop runs up to 2 padding slices that must be emptied.  sK0..sK3 are
+// the K ring slots, sV0..sV3 the V slots; each is its own LDS array, and the
+// caller passes them in by name.
+template <int D, int MODE, bool FAST, bool PAD>
+__device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile, __bf16 *sK0,
+                                               __bf16 *sK1, __bf16 *sK2, __bf16 *sK3, __bf16 *sV0,
+                                               __bf16 *sV1, __bf16 *sV2, __bf16 *sV3) {
     Tile tl;
-    if (!decode_tile(a, MODE, tl)) return;
+    if (!decode_tile(a, MODE, tile, tl)) return;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, half = lane >> 5;
-    const int r = wave * 32 + col;
     const __bf16 *__restrict__ qp = static_cast<const __bf16 *>(a.q);
     const __bf16 *__restrict__ kp = static_cast<const __bf16 *>(a.k);
     const __bf16 *__restrict__ vp = static_cast<const __bf16 *>(a.v);
+    const int nh = tl.nslice;
+    const int wfirst = tl.t0 + wave * kWaveRows;   // OWN / DENSE: the wave's first row
 
-    // this lane's query row
-    bool rvalid;
-    int t, h, slot = 0;
-    if (MODE == kPast) {
-        rvalid = r < tl.nrows;
-        const uint64_t rec = rvalid ? a.lists[tl.row_begin + r] : 0ull;
-        t = (int)row_t(rec);
-        h = tl.g * a.G + (int)row_hh(rec);
-        slot = (int)row_slot(rec);
-    } else {
-        t = tl.t0 + r;
-        rvalid = t < tl.tend;
-        h = tl.h;
-    }
-    const int tq = rvalid ? t : 0x7fffffff;    // padding rows never mask anything
-    // wave-uniform token range of the wave's rows (OWN / DENSE)
-    const int wtmin = (MODE == kPast) ? 0 : tl.t0 + wave * 32;
-    const int wtmax = (MODE == kPast) ? 0x7fffffff : min(tl.t0 + wave * 32 + 32, tl.tend) - 1;
-
-    bf16x8_t qf[D / 16];
-    if (rvalid) {
-        const __bf16 *src = qp + (((size_t)tl.b * a.S + t) * a.Hq + h) * D + half * 8;
+    // this lane's two query rows (column groups g = 0, 1)
+    bool rvalid[2];
+    int t[2], h[2], slot[2], tq[2];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t *>(src + kk * 16);
-    } else {
+    for (int g = 0; g < 2; ++g) {
+        const int r = wave * kWaveRows + g * 32 + col;
+        slot[g] = 0;
+        if (MODE == kPast) {
+            rvalid[g] = r < tl.nrows;
+            const uint64_t rec = rvalid[g] ? a.lists[tl.row_begin + r] : 0ull;
+            t[g] = (int)row_t(rec);
+            h[g] = tl.g * a.G + (int)row_hh(rec);
+            slot[g] = (int)row_slot(rec);
+        } else {
+            t[g] = tl.t0 + r;
+            rvalid[g] = t[g] < tl.tend;
+            h[g] = tl.h;
+        }
+        tq[g] = rvalid[g] ? t[g] : 0x7fffffff;    // padding rows never mask anything
+    }
+
+    // ---- K / V staging: global -> LDS directly, 1 KB (64 lanes x 16 B) per instruction
+    constexpr int CPR = D / 8;              // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;           // rows per instruction
+    constexpr int IPS = kS / RPI / 4;       // instructions per wave per slice
+    static_assert(IPS >= 1, "slice too small for the staging pattern");
+    const size_t rstride = (size_t)a.Hkv * D;
+    const __bf16 *kbase = kp + ((size_t)tl.b * a.S + tl.key_begin) * rstride + (size_t)tl.g * D;
+    const __bf16 *vbase = vp + ((size_t)tl.b * a.S + tl.key_begin) * rstride + (size_t)tl.g * D;
+    // element offsets (row * rstride + chunk * 8) this lane loads in each of its instructions
+    int ld_k[IPS], ld_v[IPS];
+#pragma unroll
+    for (int i = 0; i < IPS; ++i) {
+        const int r = (wave * IPS + i) * RPI + lane / CPR, pc = lane % CPR;
+        ld_k[i] = r * (int)rstride + ((pc ^ swz_k<D>(r)) << 3);
+        ld_v[i] = r * (int)rstride + ((pc ^ swz_v<D>(r)) << 3);
+    }
+    // slices past the last are clamped to it (loaded again, never used)
+    auto load_k = [&](int hs, __bf16 *dst) {
+        const __bf16 *src = kbase + (size_t)(min(hs, nh - 1) * kS) * rstride;
+#pragma unroll
+        for (int i = 0; i < IPS; ++i)
+            __builtin_amdgcn_global_load_lds(src + ld_k[i], (lds_void_t *)(dst + (wave * IPS + i) * 512),
+                                             16, 0, 0);
+    };
+    auto load_v = [&](int hs, __bf16 *dst) {
+        const __bf16 *src = vbase + (size_t)(min(hs, nh - 1) * kS) * rstride;
+#pragma unroll
+        for (int i = 0; i < IPS; ++i)
+            __builtin_amdgcn_global_load_lds(src + ld_v[i], (lds_void_t *)(dst + (wave * IPS + i) * 512),
+                                             16, 0, 0);
+    };
+    // the first slices start moving before Q is even loaded
+    load_k(0, sK0);
+    load_k(1, sK1);
+    load_k(2, sK2);
+    load_k(3, sK3);
+    load_v(0, sV0);
+    load_v(1, sV1);
+    load_v(2, sV2);
+
+    bf16x8_t qf[2][D / 16];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        if (rvalid[g]) {
+            const __bf16 *src = qp + (((size_t)tl.b * a.S + t[g]) * a.Hq + h[g]) * D + half * 8;
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+                qf[g][kk] = *reinterpret_cast<const bf16x8_t *>(src + kk * 16);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qf[g][kk][e] = (__bf16)0.f;
+        }
+    }
+
+    // logits become log2 units in fp32 (s * log2(e) / sqrt(d), at the exponent);
+    // qn2 = |q|^2 scaled the same way
+    const float sl2 = a.scale_log2;
+    float qn2[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        float acc = 0.f;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.f;
+            for (int e = 0; e < 8; ++e) acc = fmaf((float)qf[g][kk][e], (float)qf[g][kk][e], acc);
+        qn2[g] = (acc + __shfl_xor(acc, 32, 64)) * (sl2 * sl2);
     }
-
-    f32x16_t oacc[D / 32];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-    const float sl2 = a.scale_log2;
-
-    // ---- K / V staging: global -> registers -> LDS (V transposed on the way)
-    constexpr int KCH = kN * D / 8 / 256;          // 16-byte K chunks per thread
-    constexpr int VUN = (kN / 4) * (D / 8);        // units of 4 keys x 8 dims
-    static_assert(VUN <= 256, "one V unit per thread at most");
-    const size_t rstride = (size_t)a.Hkv * D;
-    const __bf16 *kbase = kp + ((size_t)tl.b * a.S) * rstride + (size_t)tl.g * D;
-    const __bf16 *vbase = vp + ((size_t)tl.b * a.S) * rstride + (size_t)tl.g * D;
-    const bool vact = (VUN == 256) || tid < VUN;
-    // V units: consecutive lanes take consecutive 4-key groups, so one LDS store
-    // instruction of 16 lanes fills a whole 128-byte row of the transposed tile
-    const int vkg = tid % (kN / 4), vcol = tid / (kN / 4);
-    // per-thread K chunk coordinates (chunk c = tid + 256 u)
-    const int kc0 = tid, kc1 = tid + 256, kc2 = tid + 512, kc3 = tid + 768;
-    uint4 kr0, kr1, kr2, kr3, vr0, vr1, vr2, vr3;
-
-#define MOBA_KLD(c) (*reinterpret_cast<const uint4 *>(ks + ((c) / (D / 8)) * rstride + ((c) % (D / 8)) * 8))
-#define MOBA_KST(c, x) (*reinterpret_cast<uint4 *>(&sm.k[buf][(c) / (D / 8)][((c) % (D / 8)) * 8]) = (x))
-    auto load_kv = [&](int kb) {
-        const __bf16 *ks = kbase + (size_t)kb * rstride;
-        kr0 = MOBA_KLD(kc0);
-        kr1 = MOBA_KLD(kc1);
-        if constexpr (KCH > 2) {
-            kr2 = MOBA_KLD(kc2);
-            kr3 = MOBA_KLD(kc3);
+    // largest squared key norm over the tile's key range
+    float kn2;
+    {
+        const float *km = a.kmax2 + ((size_t)tl.b * a.Hkv + tl.g) * a.n;
+        if (MODE == kDense) {
+            kn2 = 0.f;
+            for (int j = 0; j <= tl.tmax / a.B; ++j) kn2 = fmaxf(kn2, km[j]);
+        } else {
+            kn2 = km[tl.key_begin / a.B];
         }
-        if (vact) {
-            const __bf16 *vs = vbase + (size_t)(kb + vkg * 4) * rstride + vcol * 8;
-            vr0 = *reinterpret_cast<const uint4 *>(vs);
-            vr1 = *reinterpret_cast<const uint4 *>(vs + rstride);
-            vr2 = *reinterpret_cast<const uint4 *>(vs + 2 * rstride);
-            vr3 = *reinterpret_cast<const uint4 *>(vs + 3 * rstride);
+    }
+    constexpr float kBound2 = 64.f * 64.f;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's part of the first slices is in LDS
+    if constexpr (FAST) {
+        if (__syncthreads_or(!(qn2[0] * kn2 <= kBound2 && qn2[1] * kn2 <= kBound2))) {
+            if (threadIdx.x == 0) a.defer_list[atomicAdd(a.defer_count, 1u)] = tile;
+            return;
         }
-    };
-    auto store_kv = [&](int buf) {
-        MOBA_KST(kc0, kr0);
-        MOBA_KST(kc1, kr1);
-        if constexpr (KCH > 2) {
-            MOBA_KST(kc2, kr2);
-            MOBA_KST(kc3, kr3);
-        }
-        if (vact) {
-            // dims vcol*8 + 2p (low halves) and + 2p + 1 (high halves), keys vkg*4 .. +3
-            __bf16 *dst = &sm.vt[buf][vcol * 8][vt_col(vkg * 4)];
-            constexpr int VS = kN + kPad;
-            constexpr uint32_t kLo = 0x05040100u, kHi = 0x07060302u;   // v_perm byte selectors
-#define MOBA_VT(p, a0, a1, a2, a3)                                                        \
-            {                                                                             \
-                uint2 lo, hi;                                                             \
-                lo.x = __builtin_amdgcn_perm((a1), (a0), kLo);                            \
-                lo.y = __builtin_amdgcn_perm((a3), (a2), kLo);                            \
-                hi.x = __builtin_amdgcn_perm((a1), (a0), kHi);                            \
-                hi.y = __builtin_amdgcn_perm((a3), (a2), kHi);                            \
-                *reinterpret_cast<uint2 *>(dst + (2 * (p)) * VS) = lo;                    \
-                *reinterpret_cast<uint2 *>(dst + (2 * (p) + 1) * VS) = hi;                \
-            }
-            MOBA_VT(0, vr0.x, vr1.x, vr2.x, vr3.x)
-            MOBA_VT(1, vr0.y, vr1.y, vr2.y, vr3.y)
-            MOBA_VT(2, vr0.z, vr1.z, vr2.z, vr3.z)
-            MOBA_VT(3, vr0.w, vr1.w, vr2.w, vr3.w)
-#undef MOBA_VT
-        }
-    };
-#undef MOBA_KLD
-#undef MOBA_KST
-
-    load_kv(tl.key_begin);
-    store_kv(0);
-    __syncthreads();
-
-    const f32x16_t zero16 = {};
-    for (int s = 0; s < tl.nsub; ++s) {
-        const int buf = s & 1;
-        const int kb = tl.key_begin + s * kN;
-        // prefetch the next sub-tile (the last iteration re-reads the last one)
-        load_kv(tl.key_begin + min(s + 1, tl.nsub - 1) * kN);
-
-        if (MODE == kPast || kb <= wtmax) {
-            f32x16_t sacc[kN / 32];
-#pragma unroll
-            for (int kt = 0; kt < kN / 32; ++kt) {
-#pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk) {
-                    const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(
-                        &sm.k[buf][kt * 32 + col][kk * 16 + half * 8]);
-                    sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        av, qf[kk], kk == 0 ? zero16 : sacc[kt], 0, 0, 0);
-                }
-            }
-            if (MODE != kPast && kb + kN - 1 > wtmin) {
-#pragma unroll
-                for (int kt = 0; kt < kN / 32; ++kt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = kb + kt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                        if (key > tq) sacc[kt][i] = -INFINITY;
-                    }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kt = 0; kt < kN / 32; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kt][i], sacc[kt][i + 1]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
-            if (__any(mx > m_run + kRescaleSlack)) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-            }
-            float psum = 0.f;
-            bf16x8_t pb[kN / 32][2];
-#pragma unroll
-            for (int kt = 0; kt < kN / 32; ++kt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], sl2, -m_run));
-                    psum += pv;
-                    pb[kt][i >> 3][i & 7] = (__bf16)pv;
-                }
-            l_run += psum;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int kt = 0; kt < kN / 32; ++kt)
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const bf16x8_t av = *reinterpret_cast<const bf16x8_t *>(
-                            &sm.vt[buf][dt * 32 + col][kt * 32 + 16 * h2 + 8 * half]);
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kt][h2], oacc[dt], 0, 0, 0);
-                    }
-        }
-        if (s + 1 < tl.nsub) store_kv(buf ^ 1);
+    } else {
         __syncthreads();
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const float inv = 1.f / l_tot;
-    const float lse = m_run + __log2f(l_tot);
-    constexpr int LPR = D / 8;          // lanes per 256-byte (D = 128) output row
-    constexpr int RPP = 64 / LPR;       // rows per store pass
-
-    if (MODE == kPast) {
-        // normalised partial (bf16) -> LDS -> whole-row stores
-        __bf16 *stg = reinterpret_cast<__bf16 *>(smem_raw) + wave * 32 * (D + kPad);
+    f32x16_t oacc[2][D / 32];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                *reinterpret_cast<uint2 *>(stg + col * (D + kPad) + dt * 32 + 8 * g4 + 4 * half) =
-                    pack4(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv,
-                          oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
+            for (int i = 0; i < 16; ++i) oacc[g][dt][i] = 0.f;
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+    typedef f32x16_t HTile[2];     // S^T of one slice, per column group
+    typedef bf16x8_t KRegs[D / 16];        // K operand of one slice (this lane's part)
+    typedef bf16x8_t VRegs[2][D / 32];     // V^T operand of one slice (this lane's part)
+    const f32x16_t zero16 = {};
+    // K operand of the slice in ktile: lane (row, half) holds 16-byte chunks 2 kk + half of its row
+    auto read_k = [&](KRegs &kr, const __bf16 *ktile) {
+        const __bf16 *base = ktile + col * D;
+        const int sw = swz_k<D>(col);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            kr[kk] = *reinterpret_cast<const bf16x8_t *>(base + (((kk * 2 + half) ^ sw) << 3));
+    };
+    // S^T = K Q^T of one slice: rows = 32 keys, columns = queries
+    auto s_mfma = [&](HTile &sa, const KRegs &kr) {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+                sa[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kk], qf[g][kk], kk == 0 ? zero16 : sa[g],
+                                                                0, 0, 0);
+    };
+    // mask, then (when tracking the running max) the row max of slice hs.
+    // OWN / DENSE: causal mask on the slices that reach past the wave's first
+    // row; it also empties the padding slices, whose keys all lie beyond the
+    // tile's last row.  PAST: padding slices are emptied whole.
+    auto mask_max = [&](HTile &sa, int hs, float (&mx)[2], auto fast_c) {
+        const int kb = tl.key_begin + hs * kS;
+        if constexpr (MODE != kPast) {
+            if (kb + kS - 1 > wfirst) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = kb + 8 * (i >> 2) + 4 * half + (i & 3);
+                        if (key > tq[g]) sa[g][i] = -INFINITY;
+                    }
             }
-        const long long row_slot_id =
-            rvalid ? (((long long)tl.b * a.Hq + h) * a.S + t) * a.nslot + slot : -1ll;
-        if (rvalid && half == 0) a.part_lse[row_slot_id] = lse;
+        } else if constexpr (PAD) {
+            if (hs >= nh) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sa[g][i] = -INFINITY;
+            }
+        }
+        if constexpr (!decltype(fast_c)::value) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                float m = fmaxf(sa[g][0], sa[g][1]);
+#pragma unroll
+                for (int i = 2; i < 16; i += 2) m = fmaxf(m, fmaxf(sa[g][i], sa[g][i + 1]));
+                mx[g] = fmaxf(m, __shfl_xor(m, 32, 64)) * sl2;
+            }
+        }
+    };
+    auto rescale = [&](const float (&mc)[2]) {
+        if (__any(mc[0] > m_run[0] + kRescaleSlack || mc[1] > m_run[1] + kRescaleSlack)) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const float m_new = fmaxf(m_run[g], mc[g]);
+                const float alpha =
+                    (m_run[g] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - m_new);
+                m_run[g] = m_new;
+                l_run[g] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[g][dt][i] *= alpha;
+            }
+        }
+    };
+    // P = 2^(S log2(e)/sqrt(d) - m) (m = 0 on the bounded path) of column group
+    // g, in bf16 for the PV product; the row sums add the same bf16 values, two
+    // per dot2.
+    const bf16x2_t ones2 = {(__bf16)1.f, (__bf16)1.f};
+    auto exp_group = [&](const HTile &sa, int g, bf16x8_t (&pbg)[2], auto fast_c) {
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            float p0, p1;
+            if constexpr (decltype(fast_c)::value) {
+                p0 = __builtin_amdgcn_exp2f(sa[g][i] * sl2);
+                p1 = __builtin_amdgcn_exp2f(sa[g][i + 1] * sl2);
+            } else {
+                p0 = __builtin_amdgcn_exp2f(fmaf(sa[g][i], sl2, -m_run[g]));
+                p1 = __builtin_amdgcn_exp2f(fmaf(sa[g][i + 1], sl2, -m_run[g]));
+            }
+            bf16x2_t pp;
+            pp[0] = (__bf16)p0;
+            pp[1] = (__bf16)p1;
+            pbg[i >> 3][i & 7] = pp[0];
+            pbg[i >> 3][(i & 7) + 1] = pp[1];
+            l_run[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones2, l_run[g], false);
+        }
+    };
+    // V^T operand of the PV product for dims dt*32 .. +31 and the 16 keys of key
+    // group h2: lane (d, c) needs V[16 h2 + 4 c + e][d] and V[16 h2 + 8 + 4 c + e][d]
+    const int tr_g = lane >> 4, tr_j = lane & 15;
+    const int tr_row = 4 * (tr_g >> 1) + (tr_j >> 2);           // + 16 h2 (+ 8)
+    const int tr_dim = 16 * (tr_g & 1) + 4 * (tr_j & 3);        // + dt*32
+    auto read_v = [&](VRegs &vr, const __bf16 *vtile) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int r0 = 16 * h2 + tr_row;
+            const int sw = swz_v<D>(r0);                     // rows r0 and r0 + 8 share it
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const int d = dt * 32 + tr_dim;
+                const __bf16 *pl = vtile + r0 * D + (((d >> 3) ^ sw) << 3) + (d & 7);
+                const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4_t *)(pl));
+                const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (__attribute__((address_space(3))) bf16x4_t *)(pl + 8 * D));
+                vr[h2][dt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        }
+    };
+    // O^T += V^T P^T of one slice, column group g
+    auto pv_group = [&](const bf16x8_t (&pbg)[2], const VRegs &vr, int g) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+                oacc[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr[h2][dt], pbg[h2], oacc[g][dt],
+                                                                      0, 0, 0);
+    };
+
+    {
+        const std::integral_constant<bool, FAST> fast_c;
+        if (FAST) m_run[0] = m_run[1] = 0.f;
+        HTile sa, sb;
+        float mxa[2] = {0.f, 0.f}, mxb[2] = {0.f, 0.f};
+        KRegs kr;
+        read_k(kr, sK0);
+        s_mfma(sa, kr);
+        mask_max(sa, 0, mxa, fast_c);
+        read_k(kr, sK1);
+        // Step hs, S(hs) in cur, the K operand of slice hs+1 in kr:
+        //   A: S(hs+1) on the matrix cores || P(hs) of column group 0, V(hs)
+        //      read from vc
+        //   -- barrier --
+        //   B: O += V(hs)^T P(hs)^T on the matrix cores || P(hs) of group 1,
+        //      K(hs+4) -> kl and V(hs+3) -> vl start moving, the K operand of
+        //      slice hs+2 is read from kn, S(hs+1) is masked
+        // The barrier sits where every wave's loads of K(hs+2) and V(hs+1) (issued
+        // two steps back) have landed and every read of the slots that phase B
+        // refills has completed.  The last steps compute S values that nothing
+        // uses, from the clamped reloads of the last slices.
+        auto step = [&](int hs, HTile &cur, float (&mc)[2], HTile &nxt, float (&mn)[2],
+                        const __bf16 *vc, const __bf16 *kn, __bf16 *kl, __bf16 *vl) {
+            // An opaque zero added to the K slot addresses keeps them inside the
+            // loop, where the slot base folds into the LDS instruction's offset,
+            // instead of per-slot addresses hoisted into registers.
+            int z;
+            asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+            if constexpr (!FAST) rescale(mc);
+            s_mfma(nxt, kr);
+            bf16x8_t pb[2][2];
+            exp_group(cur, 0, pb[0], fast_c);
+            VRegs vr;
+            read_v(vr, vc);
+            sched_phase_a_t<D>();
+            ring_barrier<2 * IPS>();
+            read_k(kr, kn + z);
+            load_k(hs + 4, kl);
+            load_v(hs + 3, vl);
+            pv_group(pb[0], vr, 0);
+            exp_group(cur, 1, pb[1], fast_c);
+            pv_group(pb[1], vr, 1);
+            mask_max(nxt, hs + 1, mn, fast_c);
+            sched_phase_b_t<D, 2 * IPS>();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // a multiple of 4 steps, so that the loop has one exit, at the bottom
+        const int nh4 = (nh + 3) & ~3;
+        for (int hs = 0; hs < nh4; hs += 4) {
+            step(hs, sa, mxa, sb, mxb, sV0, sK2, sK0, sV3);
+            step(hs + 1, sb, mxb, sa, mxa, sV1, sK3, sK1, sV0);
+            step(hs + 2, sa, mxa, sb, mxb, sV2, sK0, sK2, sV1);
+            step(hs + 3, sb, mxb, sa, mxa, sV3, sK1, sK3, sV2);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // the clamped reloads have landed before LDS is reused
+    __syncthreads();
+
+    float inv[2], lse[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const float l_tot = l_run[g] + __shfl_xor(l_run[g], 32, 64);
+        inv[g] = 1.f / l_tot;
+        lse[g] = m_run[g] + __log2f(l_tot);
+    }
+    constexpr int LPR = D / 8;          // lanes per output row (8 elements each)
+    constexpr int RPP = 64 / LPR;       // rows per store pass
+    // per-wave staging: one K slot and one V slot (kS * D bf16 each)
+    __bf16 *stA = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sK2 : sK3;
+    __bf16 *stB = wave == 0 ? sV0 : wave == 1 ? sV1 : wave == 2 ? sV2 : sV3;
+
+    if (MODE == kPast) {
+        // normalised partial (bf16), column group g -> rows of slot g, chunk-swizzled
+        long long id[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            __bf16 *stage = g == 0 ? stA : stB;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int ch = (dt * 4 + g4) ^ (col & (CPR - 1));
+                    *reinterpret_cast<uint2 *>(stage + col * D + ch * 8 + 4 * half) =
+                        pack4(oacc[g][dt][4 * g4] * inv[g], oacc[g][dt][4 * g4 + 1] * inv[g],
+                              oacc[g][dt][4 * g4 + 2] * inv[g], oacc[g][dt][4 * g4 + 3] * inv[g]);
+                }
+            id[g] = rvalid[g] ? (((long long)tl.b * a.Hq + h[g]) * a.S + t[g]) * a.nslot + slot[g] : -1ll;
+            if (half == 0 && rvalid[g]) a.part_lse[id[g]] = lse[g];
+        }
         __syncthreads();
         __bf16 *po = static_cast<__bf16 *>(a.part_o);
-        const int lo32 = (int)(row_slot_id & 0xffffffffll), hi32 = (int)(row_slot_id >> 32);
 #pragma unroll
-        for (int it = 0; it < 32 / RPP; ++it) {
-            const int rr = it * RPP + lane / LPR, ch = lane % LPR;
-            const long long id = ((long long)__shfl(hi32, rr, 64) << 32) |
-                                 (unsigned)__shfl(lo32, rr, 64);
-            if (id >= 0)
-                *reinterpret_cast<uint4 *>(po + id * D + ch * 8) =
-                    *reinterpret_cast<const uint4 *>(stg + rr * (D + kPad) + ch * 8);
+        for (int g = 0; g < 2; ++g) {
+            const __bf16 *stage = g == 0 ? stA : stB;
+#pragma unroll
+            for (int it = 0; it < 32 / RPP; ++it) {
+                const int rr = it * RPP + lane / LPR, ch = lane % LPR;
+                const long long rid = __shfl(id[g], rr, 64);      // lane rr holds row rr
+                if (rid >= 0)
+                    *reinterpret_cast<uint4 *>(po + rid * D + ch * 8) =
+                        *reinterpret_cast<const uint4 *>(stage + rr * D + ((ch ^ (rr & (CPR - 1))) << 3));
+            }
         }
         return;
     }
 
-    // OWN / DENSE: own result (fp32) -> LDS, then merge with the past partials
-    float *stf = reinterpret_cast<float *>(smem_raw) + wave * 32 * (D + 4);
-    float *stl = reinterpret_cast<float *>(smem_raw) + 4 * 32 * (D + 4) + wave * 32;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-            *reinterpret_cast<float4 *>(stf + col * (D + 4) + dt * 32 + 8 * g4 + 4 * half) =
-                make_float4(oacc[dt][4 * g4] * inv, oacc[dt][4 * g4 + 1] * inv,
-                            oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
-    if (half == 0) stl[col] = lse;
-    __syncthreads();
+    // OWN / DENSE: own result (fp32) of one column group -> the wave's two slots
+    // (dims 0 .. D/2-1 in A, the rest in B), then merge with the past partials
+    // and write whole output rows
+    float *fA = reinterpret_cast<float *>(stA);
+    float *fB = reinterpret_cast<float *>(stB);
+    constexpr int HC = D / 8;           // 16-byte fp32 chunks per half row
+    constexpr int DTH = D / 64;         // dim groups of 32 per half row
     const __bf16 *po = static_cast<const __bf16 *>(a.part_o);
     __bf16 *outp = static_cast<__bf16 *>(a.out);
 #pragma unroll
-    for (int it = 0; it < 32 / RPP; ++it) {
-        const int rr = it * RPP + lane / LPR, ch = lane % LPR;
-        const int tr = tl.t0 + wave * 32 + rr;
-        if (tr >= tl.tend) continue;
-        float o[8];
-        const float4 x0 = *reinterpret_cast<const float4 *>(stf + rr * (D + 4) + ch * 8);
-        const float4 x1 = *reinterpret_cast<const float4 *>(stf + rr * (D + 4) + ch * 8 + 4);
-        o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
-        o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
-        if (MODE == kOwn && tl.npast > 0) {
-            const long long rid = (((long long)tl.b * a.Hq + tl.h) * a.S + tr) * a.nslot;
-            const float lo = stl[rr];
-            float mxl = lo;
-            for (int sl = 0; sl < tl.npast; ++sl) mxl = fmaxf(mxl, a.part_lse[rid + sl]);
-            const float wo = exp2f(lo - mxl);
-            float wsum = wo;
+    for (int g = 0; g < 2; ++g) {
+        if (g) __syncthreads();
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] *= wo;
-            for (int sl = 0; sl < tl.npast; ++sl) {
-                const float w = exp2f(a.part_lse[rid + sl] - mxl);
-                wsum += w;
-                float f[8];
-                unpack8(*reinterpret_cast<const uint4 *>(po + (rid + sl) * D + ch * 8), f);
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] = fmaf(w, f[e], o[e]);
+            for (int g4 = 0; g4 < 4; ++g4) {
+                float *dst = (dt / DTH) ? fB : fA;
+                const int c = ((dt % DTH) * 8 + 2 * g4 + half) ^ (col & (HC - 1));
+                *reinterpret_cast<float4 *>(dst + col * (D / 2) + c * 4) =
+                    make_float4(oacc[g][dt][4 * g4] * inv[g], oacc[g][dt][4 * g4 + 1] * inv[g],
+                                oacc[g][dt][4 * g4 + 2] * inv[g], oacc[g][dt][4 * g4 + 3] * inv[g]);
             }
-            const float iw = 1.f / wsum;
+        __syncthreads();
+#pragma unroll 2
+        for (int it = 0; it < 32 / RPP; ++it) {
+            const int rr = it * RPP + lane / LPR, ch = lane % LPR;     // row within the group
+            const float lo = __shfl(lse[g], rr, 64);
+            const int tr = wfirst + g * 32 + rr;
+            if (tr >= tl.tend) continue;
+            float o[8];
+            const float *src = (ch / (D / 16)) ? fB : fA;
+            const int c0 = 2 * (ch % (D / 16)), sw = rr & (HC - 1);
+            const float4 x0 = *reinterpret_cast<const float4 *>(src + rr * (D / 2) + ((c0 ^ sw) << 2));
+            const float4 x1 = *reinterpret_cast<const float4 *>(src + rr * (D / 2) + (((c0 + 1) ^ sw) << 2));
+            o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
+            o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
+            if (MODE == kOwn && tl.npast > 0) {
+                const long long rid = (((long long)tl.b * a.Hq + tl.h) * a.S + tr) * a.nslot;
+                float mxl = lo;
+                for (int sl = 0; sl < tl.npast; ++sl) mxl = fmaxf(mxl, a.part_lse[rid + sl]);
+                const float wo = exp2f(lo - mxl);
+                float wsum = wo;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] *= iw;
+                for (int e = 0; e < 8; ++e) o[e] *= wo;
+                for (int sl = 0; sl < tl.npast; ++sl) {
+                    const float w = exp2f(a.part_lse[rid + sl] - mxl);
+                    wsum += w;
+                    float f[8];
+                    unpack8(*reinterpret_cast<const uint4 *>(po + (rid + sl) * D + ch * 8), f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[e] = fmaf(w, f[e], o[e]);
+                }
+                const float iw = 1.f / wsum;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] *= iw;
+            }
+            *reinterpret_cast<uint4 *>(outp + (((size_t)tl.b * a.S + tr) * a.Hq + tl.h) * D + ch * 8) =
+                pack8(o);
         }
-        *reinterpret_cast<uint4 *>(outp + (((size_t)tl.b * a.S + tr) * a.Hq + tl.h) * D + ch * 8) =
-            pack8(o);
     }
 }
+
+// The ring slots are separate LDS arrays so the compiler can prove that the
+// reads of one slot never alias the direct loads into another, and does not
+// wait for those loads before reading.
+#define MOBA_RING_ARRAYS(D)                                         \
+    __shared__ __attribute__((aligned(16))) __bf16 sK0[kS * (D)];   \
+    __shared__ __attribute__((aligned(16))) __bf16 sK1[kS * (D)];   \
+    __shared__ __attribute__((aligned(16))) __bf16 sK2[kS * (D)];   \
+    __shared__ __attribute__((aligned(16))) __bf16 sK3[kS * (D)];   \
+    __shared__ __attribute__((aligned(16))) __bf16 sV0[kS * (D)];   \
+    __shared__ __attribute__((aligned(16))) __bf16 sV1[kS * (D)];   \
+    __shared__ __attribute__((aligned(16))) __bf16 sV2[kS * (D)];   \
+    __shared__ __attribute__((aligned(16))) __bf16 sV3[kS * (D)];
+
+template <int D, int MODE, bool PAD>
+__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
+    MOBA_RING_ARRAYS(D)
+    attn_bf16_tile<D, MODE, true, PAD>(a, xcd_tile(blockIdx.x, gridDim.x), sK0, sK1, sK2, sK3, sV0, sV1,
+                                  sV2, sV3);
+}
+
+// Tracking pass: a persistent grid walks the deferred tiles (normally none).
+template <int D, int MODE, bool PAD>
+__global__ __launch_bounds__(256, 1) void attn_bf16_track_kernel(AttnArgs a) {
+    MOBA_RING_ARRAYS(D)
+    const unsigned n = *a.defer_count;
+    for (unsigned i = blockIdx.x; i < n; i += gridDim.x) {
+        attn_bf16_tile<D, MODE, false, PAD>(a, a.defer_list[i], sK0, sK1, sK2, sK3, sV0, sV1, sV2, sV3);
+        __syncthreads();
+    }
+}
+
+__global__ void zero_count_kernel(unsigned *c) { *c = 0u; }
 
 // ------------------------------------------------------------------ fp32 VALU path
 //
@@ -449,7 +720,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     __shared__ float ks[kNF][D + 4];
     __shared__ float vs[kNF][D + 4];
     Tile tl;
-    if (!decode_tile(a, MODE, tl)) return;
+    if (!decode_tile(a, MODE, xcd_tile(blockIdx.x, gridDim.x), tl)) return;
     constexpr int DH = D / 2;
     const int r = threadIdx.x >> 1, dh = threadIdx.x & 1;
     const float *__restrict__ qp = static_cast<const float *>(a.q);
@@ -560,23 +831,47 @@ static AttnArgs make_args(const AttnBuffers &bf, const Problem &p) {
     a.q = bf.q; a.k = bf.k; a.v = bf.v; a.out = bf.out;
     a.part_o = bf.part_o; a.part_lse = bf.part_lse;
     a.lists = bf.lists; a.list_off = bf.list_off; a.tile_off = bf.tile_off;
+    a.kmax2 = bf.kmax2;
+    a.defer_count = bf.defer_count;
+    a.defer_list = bf.defer_list;
     a.batch = p.batch; a.S = p.S; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.B = p.B; a.n = p.n;
     a.topk = p.topk;
     a.nslot = part_slots(p);
     a.L = (long long)p.batch * p.Hkv * p.n;
     a.ntiles = 0;
+    a.M = tile_rows(p);
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.D));
     return a;
 }
 
 static unsigned round8(unsigned long long x) { return (unsigned)((x + 7) / 8 * 8); }
 
+constexpr unsigned kTrackGrid = 256;
+
+// the bounded pass, then the tracking pass over the tiles it deferred
+template <int D, int MODE, bool PAD>
+static void bf16_pair(const AttnArgs &a, unsigned grid, hipStream_t st) {
+    attn_bf16_kernel<D, MODE, PAD><<<grid, 256, 0, st>>>(a);
+    attn_bf16_track_kernel<D, MODE, PAD><<<kTrackGrid, 256, 0, st>>>(a);
+}
+
 template <int MODE>
 static hipError_t attn_launch(AttnArgs a, const Problem &p, unsigned grid, hipStream_t st) {
     if (grid == 0) return hipSuccess;
     if (p.dtype == kBF16) {
-        if (p.D == 64) attn_bf16_kernel<64, MODE><<<grid, 256, 0, st>>>(a);
-        else attn_bf16_kernel<128, MODE><<<grid, 256, 0, st>>>(a);
+        zero_count_kernel<<<1, 1, 0, st>>>(a.defer_count);
+        // PAST tiles visit B / 32 slices; the loop runs a multiple of 4
+        bool pad = false;
+        if constexpr (MODE == kPast) pad = p.B % 128 != 0;
+        if (pad) {
+            if constexpr (MODE == kPast) {
+                if (p.D == 64) bf16_pair<64, MODE, true>(a, grid, st);
+                else bf16_pair<128, MODE, true>(a, grid, st);
+            }
+        } else {
+            if (p.D == 64) bf16_pair<64, MODE, false>(a, grid, st);
+            else bf16_pair<128, MODE, false>(a, grid, st);
+        }
     } else {
         if (p.D == 64) attn_f32_kernel<64, MODE><<<grid, 256, 0, st>>>(a);
         else attn_f32_kernel<128, MODE><<<grid, 256, 0, st>>>(a);
@@ -592,14 +887,14 @@ hipError_t launch_attn_past(const AttnBuffers &bf, const Problem &p, uint64_t ti
 
 hipError_t launch_attn_own(const AttnBuffers &bf, const Problem &p, hipStream_t st) {
     AttnArgs a = make_args(bf, p);
-    const unsigned long long tpb = (p.B + kTileRows - 1) / kTileRows;
+    const unsigned long long tpb = (p.B + a.M - 1) / a.M;
     a.ntiles = (unsigned)((unsigned long long)p.batch * p.Hkv * p.n * p.G * tpb);
     return attn_launch<kOwn>(a, p, round8(a.ntiles), st);
 }
 
 hipError_t launch_attn_dense(const AttnBuffers &bf, const Problem &p, hipStream_t st) {
     AttnArgs a = make_args(bf, p);
-    const unsigned long long ntt = (p.S + kTileRows - 1) / kTileRows;
+    const unsigned long long ntt = (p.S + a.M - 1) / a.M;
     a.ntiles = (unsigned)(ntt * p.batch * p.Hq);
     return attn_launch<kDense>(a, p, round8(a.ntiles), st);
 }

@@ -168,7 +168,7 @@ hipError_t launch_index(const int32_t *idx, uint32_t *cnt, uint32_t *cursor, uin
     fill_u32_kernel<<<(unsigned)((L + 255) / 256), 256, 0, st>>>(cnt, L);
     dim3 grid((p.S + 255) / 256, p.Hq, p.batch);
     count_kernel<<<grid, 256, 0, st>>>(idx, cnt, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk);
-    scan_kernel<<<1, 1024, 0, st>>>(cnt, cursor, list_off, tile_off, L, kTileRows);
+    scan_kernel<<<1, 1024, 0, st>>>(cnt, cursor, list_off, tile_off, L, tile_rows(p));
     scatter_kernel<<<grid, 256, 0, st>>>(idx, cursor, list_off, lists, p.S, p.Hq, p.Hkv, p.G, p.B,
                                          p.n, p.topk);
     return hipGetLastError();

@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "moba.h"
 #include "moba_internal.hpp"
 
@@ -16,8 +18,8 @@ constexpr long long kMaxSeq = 1ll << 24;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-    size_t kbar = 0, poolp = 0, idx = 0, cnt = 0, cursor = 0, list_off = 0, tile_off = 0,
-           lists = 0, part_o = 0, part_lse = 0, total = 0;
+    size_t kbar = 0, kmax2 = 0, poolp = 0, pooln = 0, defer = 0, idx = 0, cnt = 0, cursor = 0,
+           list_off = 0, tile_off = 0, lists = 0, part_o = 0, part_lse = 0, total = 0;
 };
 
 // Past selections over all rows: every row in block i keeps min(topk - 1, i) past blocks.
@@ -28,6 +30,13 @@ unsigned long long past_rows(const Problem &p) {
 }
 
 size_t elem_size(const Problem &p) { return p.dtype == kBF16 ? 2 : 4; }
+
+// Upper bound on the past-block attention tiles: every list may end in a partial tile.
+unsigned long long past_tiles_upper(const Problem &p) {
+    const unsigned long long M = (unsigned long long)tile_rows(p);
+    const unsigned long long L = (unsigned long long)p.batch * p.Hkv * p.n;
+    return (past_rows(p) + M - 1) / M + L;
+}
 
 moba_status_t make_problem(int batch, int S, int Hq, int Hkv, int D, int B, int topk,
                            moba_dtype_t dt, Problem *p) {
@@ -52,16 +61,26 @@ Layout gate_layout(const Problem &p) {
     Layout l;
     size_t off = 0;
     const size_t nchunk = p.B / pool_chunk(p.B);
-    l.kbar = off; off += align_up((size_t)p.batch * p.Hkv * p.n * p.D * 4);
-    l.poolp = off; off += align_up((size_t)p.batch * p.Hkv * p.n * nchunk * p.D * 4);
+    const size_t blocks = (size_t)p.batch * p.Hkv * p.n;
+    l.kbar = off; off += align_up(blocks * p.D * 4);
+    l.kmax2 = off; off += align_up(blocks * 4);
+    l.poolp = off; off += align_up(blocks * nchunk * p.D * 4);
+    l.pooln = off; off += align_up(blocks * nchunk * 4);
     l.total = off;
     return l;
 }
 
 Layout prefill_layout(const Problem &p) {
-    if (p.dense) return Layout();   // full causal attention needs no workspace
-    Layout l = gate_layout(p);
+    Layout l = gate_layout(p);      // block means and key-norm bounds
     size_t off = l.total;
+    // deferred-tile list: a counter then one entry per tile of the largest launch
+    const unsigned long long tiles =
+        p.dense ? dense_tiles(p) : std::max(past_tiles_upper(p), own_tiles(p));
+    l.defer = off; off += align_up(256 + (size_t)tiles * 4);
+    if (p.dense) {                  // full causal attention needs nothing more
+        l.total = off;
+        return l;
+    }
     const size_t rows = (size_t)p.batch * p.Hq * p.S;
     const size_t L = (size_t)p.batch * p.Hkv * p.n;
     l.idx = off; off += align_up(rows * p.topk * 4);
@@ -87,6 +106,15 @@ hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
 moba_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOBA_OK : MOBA_ERR_HIP; }
 
+PoolBuffers pool_buffers(char *w, const Layout &l, float *kbar_out) {
+    PoolBuffers pb;
+    pb.kbar = kbar_out ? kbar_out : reinterpret_cast<float *>(w + l.kbar);
+    pb.kmax2 = reinterpret_cast<float *>(w + l.kmax2);
+    pb.partial = reinterpret_cast<float *>(w + l.poolp);
+    pb.partial_nmax = reinterpret_cast<float *>(w + l.pooln);
+    return pb;
+}
+
 struct Events {
     void *const *ev;
     hipStream_t st;
@@ -111,23 +139,29 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
         return MOBA_ERR_UNSUPPORTED;
     const Layout l = prefill_layout(p);
     if (ws_bytes < l.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
-    if (l.total > 0 && !ws) return MOBA_ERR_INVALID_ARGUMENT;
-    if (ws && !aligned(ws, kAlign)) return MOBA_ERR_UNSUPPORTED;
+    if (!ws) return MOBA_ERR_INVALID_ARGUMENT;
+    if (!aligned(ws, kAlign)) return MOBA_ERR_UNSUPPORTED;
 
     hipStream_t st = as_stream(stream);
     const Events E{events, st};
     char *w = static_cast<char *>(ws);
+    const PoolBuffers pb = pool_buffers(w, l, nullptr);
+    float *kbar = pb.kbar;
     AttnBuffers bf;
     bf.q = q; bf.k = k; bf.v = v; bf.out = out;
+    bf.kmax2 = pb.kmax2;
+    bf.defer_count = reinterpret_cast<unsigned *>(w + l.defer);
+    bf.defer_list = reinterpret_cast<unsigned *>(w + l.defer + 256);
     hipError_t e = hipSuccess;
     if (p.dense) {
-        for (int i = 0; i <= MOBA_STAGE_ATTN_PAST && e == hipSuccess; ++i) e = E.mark(i);
+        // key-norm bounds (the pool pass), then full causal attention
+        if ((e = E.mark(MOBA_STAGE_POOL)) != hipSuccess) return MOBA_ERR_HIP;
+        if ((e = launch_pool(k, pb, p, st)) != hipSuccess) return MOBA_ERR_HIP;
+        for (int i = MOBA_STAGE_GATE; i <= MOBA_STAGE_ATTN_PAST && e == hipSuccess; ++i) e = E.mark(i);
         if (e == hipSuccess) e = launch_attn_dense(bf, p, st);
         for (int i = MOBA_STAGE_ATTN_OWN; i <= MOBA_NUM_STAGES && e == hipSuccess; ++i) e = E.mark(i);
         return hip_status(e);
     }
-    float *kbar = reinterpret_cast<float *>(w + l.kbar);
-    float *poolp = reinterpret_cast<float *>(w + l.poolp);
     int32_t *idx = reinterpret_cast<int32_t *>(w + l.idx);
     uint32_t *cnt = reinterpret_cast<uint32_t *>(w + l.cnt);
     uint32_t *cursor = reinterpret_cast<uint32_t *>(w + l.cursor);
@@ -139,11 +173,10 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
     bf.lists = lists; bf.list_off = list_off; bf.tile_off = tile_off;
 
     const unsigned long long prow = past_rows(p);
-    const unsigned long long L = (unsigned long long)p.batch * p.Hkv * p.n;
-    const unsigned long long tiles_upper = (prow + kTileRows - 1) / kTileRows + L;
+    const unsigned long long tiles_upper = past_tiles_upper(p);
 
     if ((e = E.mark(MOBA_STAGE_POOL)) != hipSuccess) return MOBA_ERR_HIP;
-    if ((e = launch_pool(k, kbar, poolp, p, st)) != hipSuccess) return MOBA_ERR_HIP;
+    if ((e = launch_pool(k, pb, p, st)) != hipSuccess) return MOBA_ERR_HIP;
     if ((e = E.mark(MOBA_STAGE_GATE)) != hipSuccess) return MOBA_ERR_HIP;
     if ((e = launch_gate(q, kbar, idx, p, st)) != hipSuccess) return MOBA_ERR_HIP;
     if ((e = E.mark(MOBA_STAGE_INDEX)) != hipSuccess) return MOBA_ERR_HIP;
@@ -196,8 +229,7 @@ moba_status_t moba_pool(const void *k, float *kbar, int batch, int S, int Hkv, i
     const Layout l = gate_layout(p);
     if (ws_bytes < l.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
     char *w = static_cast<char *>(ws);
-    return hip_status(
-        launch_pool(k, kbar, reinterpret_cast<float *>(w + l.poolp), p, as_stream(stream)));
+    return hip_status(launch_pool(k, pool_buffers(w, l, kbar), p, as_stream(stream)));
 }
 
 moba_status_t moba_gate(const void *q, const void *k, int32_t *block_idx, int batch, int S,
@@ -213,10 +245,10 @@ moba_status_t moba_gate(const void *q, const void *k, int32_t *block_idx, int ba
     if (ws_bytes < l.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
     hipStream_t st = as_stream(stream);
     char *w = static_cast<char *>(ws);
-    float *kbar = reinterpret_cast<float *>(w + l.kbar);
+    const PoolBuffers pb = pool_buffers(w, l, nullptr);
     hipError_t e = hipSuccess;
-    if (!p.dense) e = launch_pool(k, kbar, reinterpret_cast<float *>(w + l.poolp), p, st);
-    if (e == hipSuccess) e = launch_gate(q, kbar, block_idx, p, st);
+    if (!p.dense) e = launch_pool(k, pb, p, st);
+    if (e == hipSuccess) e = launch_gate(q, pb.kbar, block_idx, p, st);
     return hip_status(e);
 }
 

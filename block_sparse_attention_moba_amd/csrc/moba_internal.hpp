@@ -9,8 +9,6 @@ namespace moba {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// Query rows per attention tile (4 waves x 32 rows for bf16; 128 threads x 1 row for fp32).
-constexpr int kTileRows = 128;
 // Largest number of past blocks the gate keeps per row.
 constexpr int kMaxPast = 31;
 // Block-count limit for the LDS histograms of the index build.
@@ -41,8 +39,13 @@ __device__ inline uint32_t xcd_tile(uint32_t bid, uint32_t nb) {
 }
 
 // ---- launchers (each returns the launch status) ----
-hipError_t launch_pool(const void *k, float *kbar, float *partial, const Problem &p,
-                       hipStream_t st);
+struct PoolBuffers {
+    float *kbar;           // [batch][Hkv][n][D] block means
+    float *kmax2;          // [batch][Hkv][n] largest squared key norm of each block
+    float *partial;        // [batch][Hkv][n][chunks][D] chunk sums
+    float *partial_nmax;   // [batch][Hkv][n][chunks] chunk norm maxima
+};
+hipError_t launch_pool(const void *k, const PoolBuffers &pb, const Problem &p, hipStream_t st);
 hipError_t launch_gate(const void *q, const float *kbar, int32_t *idx, const Problem &p,
                        hipStream_t st);
 hipError_t launch_index(const int32_t *idx, uint32_t *cnt, uint32_t *cursor, uint64_t *list_off,
@@ -56,11 +59,26 @@ struct AttnBuffers {
     const uint64_t *lists;
     const uint64_t *list_off;
     const uint32_t *tile_off;
+    const float *kmax2;     // [batch][Hkv][n] largest squared key norm per block
+    unsigned *defer_count;  // deferred-tile list (tiles that need running-max tracking)
+    unsigned *defer_list;
 };
 hipError_t launch_attn_past(const AttnBuffers &b, const Problem &p, uint64_t tiles_upper,
                             hipStream_t st);
 hipError_t launch_attn_own(const AttnBuffers &b, const Problem &p, hipStream_t st);
 hipError_t launch_attn_dense(const AttnBuffers &b, const Problem &p, hipStream_t st);
+
+// Query rows per attention tile: 4 waves x 64 rows on the bf16 matrix-core
+// path, 256 threads x half a row on the fp32 path.
+inline int tile_rows(const Problem &p) { return p.dtype == kBF16 ? 256 : 128; }
+
+// Tiles of each attention launch (the past-block count is an upper bound).
+inline unsigned long long own_tiles(const Problem &p) {
+    return (unsigned long long)p.batch * p.Hkv * p.n * p.G * ((p.B + tile_rows(p) - 1) / tile_rows(p));
+}
+inline unsigned long long dense_tiles(const Problem &p) {
+    return (unsigned long long)p.batch * p.Hq * ((p.S + tile_rows(p) - 1) / tile_rows(p));
+}
 
 // Partial-output slots per query row: one per selectable past block.
 inline int part_slots(const Problem &p) { return p.topk > 1 ? p.topk - 1 : 1; }

@@ -5,9 +5,11 @@
 // Two launches.  pool_partial: one workgroup per (chunk of CT tokens, block,
 // KV head, batch) streams CT x D keys with 16-byte loads (one D-row per
 // D/8 lanes, so a wave reads 64 x 16 contiguous bytes per step) and writes
-// the chunk's fp32 column sums.  pool_finalize: sums the chunk partials of a
-// block in a fixed order and divides by the block size.  No atomics, so the
-// result is bitwise reproducible.
+// the chunk's fp32 column sums and the largest squared key norm of the chunk.
+// pool_finalize: sums the chunk partials of a block in a fixed order and
+// divides by the block size, and takes the block's largest squared key norm
+// (the attention kernels bound every logit of the block by it).  No atomics,
+// so the result is bitwise reproducible.
 #include "moba_internal.hpp"
 
 namespace moba {
@@ -32,11 +34,13 @@ __device__ inline void load8(const float *p, float *f) {
 // grid (nchunk, n * Hkv, batch), 256 threads.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_partial_kernel(const T *__restrict__ k,
-                                                           float *__restrict__ partial, int S,
+                                                           float *__restrict__ partial,
+                                                           float *__restrict__ partial_nmax, int S,
                                                            int Hkv, int B, int n, int CT) {
     constexpr int LPT = D / 8;       // lanes per token row
     constexpr int TPP = 256 / LPT;   // token rows per pass
     __shared__ float red[TPP][D + 1];
+    __shared__ float redn[TPP];
     const int chunk = blockIdx.x;
     const int j = blockIdx.y / Hkv;
     const int g = blockIdx.y % Hkv;
@@ -47,27 +51,45 @@ __global__ __launch_bounds__(256) void pool_partial_kernel(const T *__restrict__
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    float nmax = 0.f;
     const int t0 = j * B + chunk * CT;
     for (int t = t0 + tr; t < t0 + CT; t += TPP) {
         float f[8];
         load8(k + (((size_t)b * S + t) * Hkv + g) * D + vec * 8, f);
+        float sq = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += f[e];
+        for (int e = 0; e < 8; ++e) {
+            acc[e] += f[e];
+            sq = fmaf(f[e], f[e], sq);
+        }
+        // squared norm of token t: sum over the LPT lanes that hold its row
+#pragma unroll
+        for (int off = 1; off < LPT; off <<= 1) sq += __shfl_xor(sq, off, LPT);
+        nmax = fmaxf(nmax, sq);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[tr][vec * 8 + e] = acc[e];
+    if (vec == 0) redn[tr] = nmax;
     __syncthreads();
+    const int nchunk = gridDim.x;
+    const size_t pc = (((size_t)b * Hkv + g) * n + j) * nchunk + chunk;
     if (tid < D) {
         float s = 0.f;
         for (int r = 0; r < TPP; ++r) s += red[r][tid];
-        const int nchunk = gridDim.x;
-        partial[((((size_t)b * Hkv + g) * n + j) * nchunk + chunk) * D + tid] = s;
+        partial[pc * D + tid] = s;
+    }
+    if (tid == 0) {
+        float m = 0.f;
+        for (int r = 0; r < TPP; ++r) m = fmaxf(m, redn[r]);
+        partial_nmax[pc] = m;
     }
 }
 
 // grid (ceil(batch * Hkv * n * D / 256)), 256 threads: one output element each.
 __global__ __launch_bounds__(256) void pool_finalize_kernel(const float *__restrict__ partial,
+                                                            const float *__restrict__ partial_nmax,
                                                             float *__restrict__ kbar,
+                                                            float *__restrict__ kmax2,
                                                             long long total, int D, int nchunk,
                                                             int B) {
     const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -78,29 +100,31 @@ __global__ __launch_bounds__(256) void pool_finalize_kernel(const float *__restr
     float s = 0.f;
     for (int c = 0; c < nchunk; ++c) s += src[(size_t)c * D];
     kbar[e] = s / (float)B;
+    if (i == 0) {
+        float m = 0.f;
+        for (int c = 0; c < nchunk; ++c) m = fmaxf(m, partial_nmax[(size_t)blk * nchunk + c]);
+        kmax2[blk] = m;
+    }
 }
 
 template <typename T, int D>
-static hipError_t pool_impl(const void *k, float *kbar, float *partial, const Problem &p,
+static hipError_t pool_impl(const void *k, const PoolBuffers &pb, const Problem &p,
                             hipStream_t st) {
     const int CT = pool_chunk(p.B);
     const int nchunk = p.B / CT;
     dim3 grid(nchunk, p.n * p.Hkv, p.batch);
-    pool_partial_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T *>(k), partial, p.S,
-                                                    p.Hkv, p.B, p.n, CT);
+    pool_partial_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T *>(k), pb.partial,
+                                                    pb.partial_nmax, p.S, p.Hkv, p.B, p.n, CT);
     const long long total = (long long)p.batch * p.Hkv * p.n * D;
-    pool_finalize_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(partial, kbar, total, D,
-                                                                         nchunk, p.B);
+    pool_finalize_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(
+        pb.partial, pb.partial_nmax, pb.kbar, pb.kmax2, total, D, nchunk, p.B);
     return hipGetLastError();
 }
 
-hipError_t launch_pool(const void *k, float *kbar, float *partial, const Problem &p,
-                       hipStream_t st) {
+hipError_t launch_pool(const void *k, const PoolBuffers &pb, const Problem &p, hipStream_t st) {
     if (p.dtype == kBF16)
-        return p.D == 64 ? pool_impl<__bf16, 64>(k, kbar, partial, p, st)
-                         : pool_impl<__bf16, 128>(k, kbar, partial, p, st);
-    return p.D == 64 ? pool_impl<float, 64>(k, kbar, partial, p, st)
-                     : pool_impl<float, 128>(k, kbar, partial, p, st);
+        return p.D == 64 ? pool_impl<__bf16, 64>(k, pb, p, st) : pool_impl<__bf16, 128>(k, pb, p, st);
+    return p.D == 64 ? pool_impl<float, 64>(k, pb, p, st) : pool_impl<float, 128>(k, pb, p, st);
 }
 
 }  // namespace moba

@@ -65,10 +65,11 @@ def test_workspace_size_validation(args, code):
 def test_workspace_sizes():
     rc, pb, gb = ws_size(1, 1024, 2, 2, 64, 128, 3, F32)
     assert rc == 0 and pb > gb > 0
-    rc, pb, gb = ws_size(1, 1024, 2, 2, 64, 128, 8, F32)   # topk >= n: full attention
-    assert rc == 0 and pb == 0
-    rc, pb2, _ = ws_size(1, 64 * 64, 2, 2, 64, 64, 40 + 24, BF16)
-    assert rc == 0 and pb2 == 0                              # dense again: no topk limit
+    # topk >= n: full attention needs only the key-norm pass and the deferred-tile list
+    rc, pb, gb = ws_size(1, 1024, 2, 2, 64, 128, 8, F32)
+    assert rc == 0 and gb < pb < gb + (1 << 16)
+    rc, pb2, gb2 = ws_size(1, 64 * 64, 2, 2, 64, 64, 40 + 24, BF16)
+    assert rc == 0 and gb2 < pb2 < gb2 + (1 << 16)           # dense again: no topk limit
     # the 1M-token workload fits one 288 GB GPU with its inputs
     rc, pb, _ = ws_size(1, 1 << 20, 32, 8, 128, 4096, 12, BF16)
     assert rc == 0 and 50e9 < pb < 200e9
