@@ -1,10 +1,8 @@
-// Block-sparse attention over the selected KV blocks, with the online-softmax
-// merge of the partial outputs fused into the own-block pass (write-up "MoBA:
-// Mixture of Block Attention", implementation steps three to five: per-KV-
+// Block-sparse attention over the selected KV blocks (write-up "MoBA:
+// Mixture of Block Attention", implementation steps three and four: per-KV-
 // block attention of the queries assigned to it, outputs put back in query
-// order, and an online-softmax merge because a query attends its current
-// block plus several history blocks; Taiwan AI overview, section
-// "技術細節與優勢": the own block is always attended, causally).
+// order; Taiwan AI overview, section "技術細節與優勢": the own block is always
+// attended, causally).  The online-softmax merge of step five is in merge.hip.
 //
 // Three tile kinds share one kernel body:
 //   PAST  : up to M listed query rows of one (batch, KV head, past block j)
@@ -12,15 +10,15 @@
 //           normalised partial output plus its base-2 log-sum-exp to the
 //           row's slot of the partial buffer;
 //   OWN   : M consecutive query rows of one head attend their own block
-//           causally (mask only on the sub-tiles that cross the diagonal),
-//           then merge with the row's past-block partials and write the
-//           final output;
+//           causally (mask only on the slices that cross the diagonal) and
+//           write the own-block partial, or the final output when the rows
+//           have no past blocks;
 //   DENSE : M consecutive query rows attend every key <= t and write the
 //           final output (full causal attention, used when every causal block
 //           is selected).
 // M is 256 for bf16 (matrix-core path below) and 128 for fp32 (vector path).
-// Results leave through LDS so that every global store writes whole 16-byte
-// pieces of contiguous rows.
+// On the bf16 path results leave through LDS so that every global store
+// writes whole 16-byte pieces of contiguous rows.
 #include <math.h>
 
 #include <type_traits>
@@ -570,105 +568,53 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         inv[g] = 1.f / l_tot;
         lse[g] = m_run[g] + __log2f(l_tot);
     }
-    constexpr int LPR = D / 8;          // lanes per output row (8 elements each)
+    // Destination of each row: a partial slot with its log-sum-exp (past
+    // blocks; the own block of a row that has past blocks to merge with), or
+    // the output row.  The normalised rows (bf16) pass through the wave's two
+    // LDS slots, column group g in slot g, chunk-swizzled, so that every global
+    // store writes whole 16-byte pieces of contiguous rows.
+    constexpr int LPR = D / 8;          // lanes per row (8 elements each)
     constexpr int RPP = 64 / LPR;       // rows per store pass
-    // per-wave staging: one K slot and one V slot (kS * D bf16 each)
     __bf16 *stA = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sK2 : sK3;
     __bf16 *stB = wave == 0 ? sV0 : wave == 1 ? sV1 : wave == 2 ? sV2 : sV3;
-
-    if (MODE == kPast) {
-        // normalised partial (bf16), column group g -> rows of slot g, chunk-swizzled
-        long long id[2];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            __bf16 *stage = g == 0 ? stA : stB;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int ch = (dt * 4 + g4) ^ (col & (CPR - 1));
-                    *reinterpret_cast<uint2 *>(stage + col * D + ch * 8 + 4 * half) =
-                        pack4(oacc[g][dt][4 * g4] * inv[g], oacc[g][dt][4 * g4 + 1] * inv[g],
-                              oacc[g][dt][4 * g4 + 2] * inv[g], oacc[g][dt][4 * g4 + 3] * inv[g]);
-                }
-            id[g] = rvalid[g] ? (((long long)tl.b * a.Hq + h[g]) * a.S + t[g]) * a.nslot + slot[g] : -1ll;
-            if (half == 0 && rvalid[g]) a.part_lse[id[g]] = lse[g];
-        }
-        __syncthreads();
-        __bf16 *po = static_cast<__bf16 *>(a.part_o);
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const __bf16 *stage = g == 0 ? stA : stB;
-#pragma unroll
-            for (int it = 0; it < 32 / RPP; ++it) {
-                const int rr = it * RPP + lane / LPR, ch = lane % LPR;
-                const long long rid = __shfl(id[g], rr, 64);      // lane rr holds row rr
-                if (rid >= 0)
-                    *reinterpret_cast<uint4 *>(po + rid * D + ch * 8) =
-                        *reinterpret_cast<const uint4 *>(stage + rr * D + ((ch ^ (rr & (CPR - 1))) << 3));
-            }
-        }
-        return;
-    }
-
-    // OWN / DENSE: own result (fp32) of one column group -> the wave's two slots
-    // (dims 0 .. D/2-1 in A, the rest in B), then merge with the past partials
-    // and write whole output rows
-    float *fA = reinterpret_cast<float *>(stA);
-    float *fB = reinterpret_cast<float *>(stB);
-    constexpr int HC = D / 8;           // 16-byte fp32 chunks per half row
-    constexpr int DTH = D / 64;         // dim groups of 32 per half row
-    const __bf16 *po = static_cast<const __bf16 *>(a.part_o);
-    __bf16 *outp = static_cast<__bf16 *>(a.out);
+    const bool to_part = MODE == kPast || (MODE == kOwn && tl.npast > 0);
+    long long dst[2];                   // element offset of the row's destination, -1: padding
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-        if (g) __syncthreads();
+        __bf16 *stage = g == 0 ? stA : stB;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                float *dst = (dt / DTH) ? fB : fA;
-                const int c = ((dt % DTH) * 8 + 2 * g4 + half) ^ (col & (HC - 1));
-                *reinterpret_cast<float4 *>(dst + col * (D / 2) + c * 4) =
-                    make_float4(oacc[g][dt][4 * g4] * inv[g], oacc[g][dt][4 * g4 + 1] * inv[g],
-                                oacc[g][dt][4 * g4 + 2] * inv[g], oacc[g][dt][4 * g4 + 3] * inv[g]);
+                const int ch = (dt * 4 + g4) ^ (col & (CPR - 1));
+                *reinterpret_cast<uint2 *>(stage + col * D + ch * 8 + 4 * half) =
+                    pack4(oacc[g][dt][4 * g4] * inv[g], oacc[g][dt][4 * g4 + 1] * inv[g],
+                          oacc[g][dt][4 * g4 + 2] * inv[g], oacc[g][dt][4 * g4 + 3] * inv[g]);
             }
-        __syncthreads();
-#pragma unroll 2
+        dst[g] = -1;
+        if (rvalid[g]) {
+            if (to_part) {
+                const int sl = MODE == kPast ? slot[g] : a.nslot - 1;
+                const long long id = (((long long)tl.b * a.Hq + h[g]) * a.S + t[g]) * a.nslot + sl;
+                dst[g] = id * D;
+                if (half == 0) a.part_lse[id] = lse[g];
+            } else {
+                dst[g] = (((long long)tl.b * a.S + t[g]) * a.Hq + h[g]) * D;
+            }
+        }
+    }
+    __syncthreads();
+    __bf16 *base = static_cast<__bf16 *>(to_part ? a.part_o : a.out);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const __bf16 *stage = g == 0 ? stA : stB;
+#pragma unroll
         for (int it = 0; it < 32 / RPP; ++it) {
-            const int rr = it * RPP + lane / LPR, ch = lane % LPR;     // row within the group
-            const float lo = __shfl(lse[g], rr, 64);
-            const int tr = wfirst + g * 32 + rr;
-            if (tr >= tl.tend) continue;
-            float o[8];
-            const float *src = (ch / (D / 16)) ? fB : fA;
-            const int c0 = 2 * (ch % (D / 16)), sw = rr & (HC - 1);
-            const float4 x0 = *reinterpret_cast<const float4 *>(src + rr * (D / 2) + ((c0 ^ sw) << 2));
-            const float4 x1 = *reinterpret_cast<const float4 *>(src + rr * (D / 2) + (((c0 + 1) ^ sw) << 2));
-            o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
-            o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
-            if (MODE == kOwn && tl.npast > 0) {
-                const long long rid = (((long long)tl.b * a.Hq + tl.h) * a.S + tr) * a.nslot;
-                float mxl = lo;
-                for (int sl = 0; sl < tl.npast; ++sl) mxl = fmaxf(mxl, a.part_lse[rid + sl]);
-                const float wo = exp2f(lo - mxl);
-                float wsum = wo;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] *= wo;
-                for (int sl = 0; sl < tl.npast; ++sl) {
-                    const float w = exp2f(a.part_lse[rid + sl] - mxl);
-                    wsum += w;
-                    float f[8];
-                    unpack8(*reinterpret_cast<const uint4 *>(po + (rid + sl) * D + ch * 8), f);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) o[e] = fmaf(w, f[e], o[e]);
-                }
-                const float iw = 1.f / wsum;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o[e] *= iw;
-            }
-            *reinterpret_cast<uint4 *>(outp + (((size_t)tl.b * a.S + tr) * a.Hq + tl.h) * D + ch * 8) =
-                pack8(o);
+            const int rr = it * RPP + lane / LPR, ch = lane % LPR;
+            const long long o = __shfl(dst[g], rr, 64);       // lane rr holds row rr
+            if (o >= 0)
+                *reinterpret_cast<uint4 *>(base + o + ch * 8) =
+                    *reinterpret_cast<const uint4 *>(stage + rr * D + ((ch ^ (rr & (CPR - 1))) << 3));
         }
     }
 }
@@ -711,7 +657,7 @@ __global__ void zero_count_kernel(unsigned *c) { *c = 0u; }
 // fp32 inputs keep fp32 end to end (no matrix-core rounding).  Two threads
 // share a query row, each holding half of the head dimensions; the partial
 // dot products meet through one lane exchange.  Keys stream through LDS in
-// sub-tiles of 32.  The own-block pass merges the past partials of its row.
+// sub-tiles of 32.
 
 constexpr int kNF = 32;
 
@@ -792,36 +738,18 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     const float inv = 1.f / l_run;
     const float lse = m_run + log2f(l_run);
     const long long row_id = ((long long)tl.b * a.Hq + h) * a.S + t;
-    if (MODE == kPast) {
-        float *dst = static_cast<float *>(a.part_o) + (row_id * a.nslot + slot) * D + dh * DH;
+    // a partial slot (past blocks; the own block of a row with past blocks) or the output row
+    if (MODE == kPast || (MODE == kOwn && tl.npast > 0)) {
+        const int sl = MODE == kPast ? slot : a.nslot - 1;
+        float *dst = static_cast<float *>(a.part_o) + (row_id * a.nslot + sl) * D + dh * DH;
 #pragma unroll
         for (int i = 0; i < DH; ++i) dst[i] = o[i] * inv;
-        if (dh == 0) a.part_lse[row_id * a.nslot + slot] = lse;
+        if (dh == 0) a.part_lse[row_id * a.nslot + sl] = lse;
         return;
-    }
-#pragma unroll
-    for (int i = 0; i < DH; ++i) o[i] *= inv;
-    if (MODE == kOwn && tl.npast > 0) {
-        const float *ls = a.part_lse + row_id * a.nslot;
-        float mxl = lse;
-        for (int sl = 0; sl < tl.npast; ++sl) mxl = fmaxf(mxl, ls[sl]);
-        const float wo = exp2f(lse - mxl);
-        float wsum = wo;
-#pragma unroll
-        for (int i = 0; i < DH; ++i) o[i] *= wo;
-        for (int sl = 0; sl < tl.npast; ++sl) {
-            const float w = exp2f(ls[sl] - mxl);
-            wsum += w;
-            const float *src = static_cast<const float *>(a.part_o) + (row_id * a.nslot + sl) * D + dh * DH;
-#pragma unroll
-            for (int i = 0; i < DH; ++i) o[i] = fmaf(w, src[i], o[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < DH; ++i) o[i] /= wsum;
     }
     float *dst = static_cast<float *>(a.out) + (((size_t)tl.b * a.S + t) * a.Hq + h) * D + dh * DH;
 #pragma unroll
-    for (int i = 0; i < DH; ++i) dst[i] = o[i];
+    for (int i = 0; i < DH; ++i) dst[i] = o[i] * inv;
 }
 
 // ------------------------------------------------------------------ launchers

@@ -67,6 +67,7 @@ hipError_t launch_attn_past(const AttnBuffers &b, const Problem &p, uint64_t til
                             hipStream_t st);
 hipError_t launch_attn_own(const AttnBuffers &b, const Problem &p, hipStream_t st);
 hipError_t launch_attn_dense(const AttnBuffers &b, const Problem &p, hipStream_t st);
+hipError_t launch_merge(const AttnBuffers &b, const Problem &p, hipStream_t st);
 
 // Query rows per attention tile: 4 waves x 64 rows on the bf16 matrix-core
 // path, 256 threads x half a row on the fp32 path.
@@ -80,8 +81,10 @@ inline unsigned long long dense_tiles(const Problem &p) {
     return (unsigned long long)p.batch * p.Hq * ((p.S + tile_rows(p) - 1) / tile_rows(p));
 }
 
-// Partial-output slots per query row: one per selectable past block.
-inline int part_slots(const Problem &p) { return p.topk > 1 ? p.topk - 1 : 1; }
+// Partial-output slots per query row: one per selectable past block, then
+// one for the own block (slot topk - 1), which is written only when the row
+// has past blocks to merge with.
+inline int part_slots(const Problem &p) { return p.topk; }
 
 // Pool partial-sum chunk length (tokens) for a block size that is a multiple of 64.
 inline int pool_chunk(int B) { return (B % 256 == 0) ? 256 : (B % 128 == 0 ? 128 : 64); }

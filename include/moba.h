@@ -81,8 +81,8 @@ enum {
     MOBA_STAGE_INDEX = 2,    /* per-(KV head, block) lists of the query rows      */
     MOBA_STAGE_ATTN_PAST = 3,/* attention of listed rows over one past block each */
     MOBA_STAGE_ATTN_OWN = 4, /* causal attention over each query's own block,
-                                fused with the online-softmax merge of the
-                                partial outputs                                   */
+                                then the online-softmax merge of the partial
+                                outputs                                           */
     MOBA_NUM_STAGES = 5
 };
 
