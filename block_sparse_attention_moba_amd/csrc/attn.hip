@@ -140,14 +140,13 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, T
 // The V swizzle (chunk ^ {0, 4, 10, 14}[row mod 4]) keeps both 16-lane and
 // 32-lane servicing of those reads conflict-free.
 //
-// The MFMA yields raw q.k in fp32; the softmax scale log2(e)/sqrt(d) is
-// applied in fp32 at the exponent, so logits are in log2 units there.  Every
-// logit of a tile is bounded by |q| * max|k| (Cauchy-Schwarz, max|k| per
-// block from the pool pass).  When that bound, in log2 units, is <= 64 for
-// every row of the tile, 2^s can neither overflow nor underflow, so the
-// softmax runs against a fixed reference of 0: no row max, no rescale, no
-// subtraction.  Otherwise the tile goes to the tracking pass, which keeps a
-// running max (moved lazily, only when a row max exceeds it by more than 2^8).
+// Logits are taken in log2 units (scaled by log2(e)/sqrt(d)).  Every logit of
+// a tile is bounded by |q| * max|k| (Cauchy-Schwarz, max|k| per block from
+// the pool pass).  When that bound is <= 64 for every row of the tile, 2^s can
+// neither overflow nor underflow, so the softmax runs against a fixed
+// reference of 0: no row max, no rescale, no subtraction.  Otherwise the tile
+// goes to the tracking pass, which keeps a running max (moved lazily, only
+// when a row max exceeds it by more than 2^8).
 
 constexpr int kWaveRows = 64;
 constexpr int kS = 32;                 // keys per slice
@@ -203,37 +202,6 @@ __device__ __forceinline__ void ring_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// Instruction interleave of the two phases of a pipeline step (scheduler
-// groups: 0x008 matrix-core ops, 0x100 LDS reads, 0x010 global memory,
-// 0x402 vector ALU incl. transcendental).  Phase A: each S MFMA with one V^T
-// read and a share of the exponentials.  Phase B: the K operand reads first,
-// then each PV MFMA with the staging loads and the rest of the exponentials.
-#define MOBA_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
-template <int D>
-__device__ __forceinline__ void sched_phase_a_t() {
-#pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-        MOBA_SCHED(0x008, 1);
-        MOBA_SCHED(0x100, 1);
-        MOBA_SCHED(0x002, 3);
-    }
-}
-template <int D, int NLOAD>
-__device__ __forceinline__ void sched_phase_b_t() {
-    MOBA_SCHED(0x100, D / 16);             // K operand reads first
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) {     // PV of group 0 || P of group 1, loads
-        MOBA_SCHED(0x008, 1);
-        if (i < NLOAD) MOBA_SCHED(0x010, 1);
-        MOBA_SCHED(0x002, 4);
-    }
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i) {     // PV of group 1
-        MOBA_SCHED(0x008, 1);
-        MOBA_SCHED(0x002, 2);
-    }
-}
-
 // One tile.  FAST: the bounded softmax; a tile whose bound fails is appended
 // to the deferred list and left to the tracking pass.  !FAST: running-max
 // tracking.  PAD (PAST only): the block's slice count is not a multiple of 4,
@@ -248,7 +216,7 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     if (!decode_tile(a, MODE, tile, tl)) return;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave: scalar
     const int col = lane & 31, half = lane >> 5;
     const __bf16 *__restrict__ qp = static_cast<const __bf16 *>(a.q);
     const __bf16 *__restrict__ kp = static_cast<const __bf16 *>(a.k);
@@ -283,15 +251,19 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     constexpr int IPS = kS / RPI / 4;       // instructions per wave per slice
     static_assert(IPS >= 1, "slice too small for the staging pattern");
     const size_t rstride = (size_t)a.Hkv * D;
-    const __bf16 *kbase = kp + ((size_t)tl.b * a.S + tl.key_begin) * rstride + (size_t)tl.g * D;
-    const __bf16 *vbase = vp + ((size_t)tl.b * a.S + tl.key_begin) * rstride + (size_t)tl.g * D;
+    const size_t kvoff = ((size_t)tl.b * a.S + tl.key_begin) * rstride + (size_t)tl.g * D;
+    // uniform across the workgroup: kept in scalar registers for the loads' base
+    const size_t kvoff_u = ((size_t)__builtin_amdgcn_readfirstlane((unsigned)(kvoff >> 32)) << 32) |
+                           (unsigned)__builtin_amdgcn_readfirstlane((unsigned)kvoff);
+    const __bf16 *kbase = kp + kvoff_u;
+    const __bf16 *vbase = vp + kvoff_u;
     // element offsets (row * rstride + chunk * 8) this lane loads in each of its instructions
-    int ld_k[IPS], ld_v[IPS];
+    unsigned ld_k[IPS], ld_v[IPS];
 #pragma unroll
     for (int i = 0; i < IPS; ++i) {
         const int r = (wave * IPS + i) * RPI + lane / CPR, pc = lane % CPR;
-        ld_k[i] = r * (int)rstride + ((pc ^ swz_k<D>(r)) << 3);
-        ld_v[i] = r * (int)rstride + ((pc ^ swz_v<D>(r)) << 3);
+        ld_k[i] = (unsigned)(r * (int)rstride + ((pc ^ swz_k<D>(r)) << 3));
+        ld_v[i] = (unsigned)(r * (int)rstride + ((pc ^ swz_v<D>(r)) << 3));
     }
     // slices past the last are clamped to it (loaded again, never used)
     auto load_k = [&](int hs, __bf16 *dst) {
@@ -333,8 +305,11 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         }
     }
 
-    // logits become log2 units in fp32 (s * log2(e) / sqrt(d), at the exponent);
-    // qn2 = |q|^2 scaled the same way
+    // Logits in log2 units.  Bounded pass: q <- rne(q * log2(e) / sqrt(d)) in
+    // bf16, so the MFMA yields them directly (the bound keeps |s| <= 64, where
+    // this rounding moves a logit by far less than the bf16 rounding of P).
+    // Tracking pass: raw q, the scale applied in fp32 at the exponent, exact for
+    // logits of any size.  qn2 = |q|^2 in the same units.
     const float sl2 = a.scale_log2;
     float qn2[2];
 #pragma unroll
@@ -343,8 +318,16 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaf((float)qf[g][kk][e], (float)qf[g][kk][e], acc);
-        qn2[g] = (acc + __shfl_xor(acc, 32, 64)) * (sl2 * sl2);
+            for (int e = 0; e < 8; ++e) {
+                if constexpr (FAST) {
+                    const __bf16 x = (__bf16)((float)qf[g][kk][e] * sl2);
+                    qf[g][kk][e] = x;
+                    acc = fmaf((float)x, (float)x, acc);
+                } else {
+                    acc = fmaf((float)qf[g][kk][e], (float)qf[g][kk][e], acc);
+                }
+            }
+        qn2[g] = (acc + __shfl_xor(acc, 32, 64)) * (FAST ? 1.f : sl2 * sl2);
     }
     // largest squared key norm over the tile's key range
     float kn2;
@@ -448,17 +431,17 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
             }
         }
     };
-    // P = 2^(S log2(e)/sqrt(d) - m) (m = 0 on the bounded path) of column group
-    // g, in bf16 for the PV product; the row sums add the same bf16 values, two
-    // per dot2.
+    // P = 2^(S - m) (bounded pass: m = 0, S already scaled; tracking pass: the
+    // scale folded into the FMA) of column group g, in bf16 for the PV product;
+    // the row sums add the same bf16 values, two per dot2.
     const bf16x2_t ones2 = {(__bf16)1.f, (__bf16)1.f};
     auto exp_group = [&](const HTile &sa, int g, bf16x8_t (&pbg)[2], auto fast_c) {
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
             float p0, p1;
             if constexpr (decltype(fast_c)::value) {
-                p0 = __builtin_amdgcn_exp2f(sa[g][i] * sl2);
-                p1 = __builtin_amdgcn_exp2f(sa[g][i + 1] * sl2);
+                p0 = __builtin_amdgcn_exp2f(sa[g][i]);
+                p1 = __builtin_amdgcn_exp2f(sa[g][i + 1]);
             } else {
                 p0 = __builtin_amdgcn_exp2f(fmaf(sa[g][i], sl2, -m_run[g]));
                 p1 = __builtin_amdgcn_exp2f(fmaf(sa[g][i + 1], sl2, -m_run[g]));
@@ -537,7 +520,6 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
             exp_group(cur, 0, pb[0], fast_c);
             VRegs vr;
             read_v(vr, vc);
-            sched_phase_a_t<D>();
             ring_barrier<2 * IPS>();
             read_k(kr, kn + z);
             load_k(hs + 4, kl);
@@ -546,7 +528,6 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
             exp_group(cur, 1, pb[1], fast_c);
             pv_group(pb[1], vr, 1);
             mask_max(nxt, hs + 1, mn, fast_c);
-            sched_phase_b_t<D, 2 * IPS>();
             __builtin_amdgcn_sched_barrier(0);
         };
         // a multiple of 4 steps, so that the loop has one exit, at the bottom

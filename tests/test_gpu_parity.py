@@ -139,17 +139,21 @@ def test_every_block_selected_is_full_causal_attention(cfg, dev):
     assert srep["trivial"] == len(rows)
 
 
-@pytest.mark.parametrize("cfg", [
-    small("large-logits-sparse", hq=4, hkv=2, seqlen=1024, block_size=128, topk=3),
-    small("large-logits-block192", hq=2, hkv=1, seqlen=1152, block_size=192, topk=3),
-    small("large-logits-dense", hq=2, hkv=2, seqlen=768, block_size=128, topk=6),
-], ids=lambda c: c.name)
-def test_large_logits_take_the_tracking_path(cfg, dev):
-    """q and k scaled by 32 (exact in bf16): the logit bound |q| max|k| fails on
-    most tiles, so they run the running-max pass instead of the bounded one."""
-    log(f"case {cfg.name}")
+@pytest.mark.parametrize("cfg,scale", [
+    (small("large-logits-sparse", hq=4, hkv=2, seqlen=1024, block_size=128, topk=3), 32),
+    (small("large-logits-block192", hq=2, hkv=1, seqlen=1152, block_size=192, topk=3), 32),
+    (small("large-logits-dense", hq=2, hkv=2, seqlen=768, block_size=128, topk=6), 32),
+    (small("bounded-logits-to-25", hq=4, hkv=2, seqlen=1024, block_size=128, topk=3), 8),
+    (small("mixed-bounded-and-tracked", hq=4, hkv=2, seqlen=1024, block_size=128, topk=3), 12),
+], ids=lambda c: c.name if hasattr(c, "name") else f"x{c}")
+def test_logit_range_bounded_and_tracking_passes(cfg, scale, dev):
+    """q and k scaled by a power of two (exact in bf16).  x32: the logit bound
+    |q| max|k| fails on every tile, so all run the running-max pass.  x8: every
+    tile stays on the bounded pass with logits up to about 25 (log2 units).
+    x12: a few tiles exceed the bound and are deferred from the same launch."""
+    log(f"case {cfg.name} scale {scale}")
     inp = make_inputs(cfg)
-    inp = {"q": inp["q"] * 32, "k": inp["k"] * 32, "v": inp["v"]}
+    inp = {"q": inp["q"] * scale, "k": inp["k"] * scale, "v": inp["v"]}
     out, idx = run_gpu(cfg, inp, dev)
     rows = oracle.all_rows(cfg.batch, cfg.hq, cfg.seqlen)
     check_rows(cfg, host_arrays(inp), out, idx, rows)
