@@ -249,7 +249,7 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seqlen,
                    "num_q_heads": cfg.hq, "num_kv_heads": cfg.hkv, "head_dim": cfg.head_dim,
                    "block_size": cfg.block_size, "topk": cfg.topk, "parallelism": "single-gpu"},
-        "roofline": {"kernel": "attn_bf16_kernel<128, PAST> (past-block attention)",
+        "roofline": {"kernel": "attn_bf16_kernel<128, 0, false> (past-block attention)",
                      "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
                      "traffic": traffic_for(cfg.name),
