@@ -115,11 +115,11 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, T
 
 // ------------------------------------------------------------------ bf16 MFMA path
 //
-// One workgroup = 4 waves = 256 query rows.  Each wave owns 64 rows as two
-// 32-query column groups, so every K or V^T operand read from LDS feeds two
-// MFMAs.  One wave per SIMD (512 registers), so O stays in accumulation
-// registers.  Keys are consumed in slices of 32.  Step h pairs the matrix-core
-// work of one slice with the vector work of the previous one:
+// One workgroup = 256 query rows: 8 waves of 32 rows for d = 128 (two waves
+// per SIMD, up to 256 registers each), 4 waves of 64 rows (two 32-query column
+// groups, so every K or V^T operand read from LDS feeds two MFMAs) for d = 64.
+// Keys are consumed in slices of 32.  Step h pairs the matrix-core work of one
+// slice with the vector work of the previous one:
 //   S(h+1) = K(h+1) Q^T    (matrix cores)
 //   P(h) = 2^(S(h) - m), row sums, O += V(h)^T P(h)^T
 //   mask and row max of S(h+1), so that step h+1 knows whether its running
@@ -128,8 +128,8 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, T
 // K and V travel from global memory straight into LDS (global_load_lds, 16
 // bytes per lane, no registers) as row-major [key][d] slices whose 16-byte
 // chunks are XOR-swizzled per row.  Both rings have 4 slots: step h reads
-// K(h+1) and V(h) while K(h+3) and V(h+2) are in flight, so every load has two
-// steps to land.  The compiler must see that no read aliases a load in
+// V(h) and the K operand of slice h+2 while K(h+4) and V(h+3) start loading,
+// so every load has about two steps to land.  The compiler must see that no read aliases a load in
 // flight, or it waits for the load before the read, so every slot is its own
 // LDS array and the loop is unrolled by 4 with the slots named at each step.
 // K operand rows are single 16-byte reads (swizzle: row mod 16).  The V^T
@@ -148,7 +148,13 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, T
 // goes to the tracking pass, which keeps a running max (moved lazily, only
 // when a row max exceeds it by more than 2^8).
 
-constexpr int kWaveRows = 64;
+// Waves per workgroup (rows per wave = 256 / NW, in 32-row column groups).
+// d = 128: 8 waves of 32 rows, two per SIMD, so one wave's matrix-core work
+// overlaps the other's vector work (measured: same past-block speed, own-block
+// pass 13% faster than 4 waves of 64 rows).  d = 64: 4 waves of 64 rows (the
+// 32-key slice staging needs at least 64 lanes x 16 B per wave).
+template <int D>
+constexpr int attn_waves() { return D == 128 ? 8 : 4; }
 constexpr int kS = 32;                 // keys per slice
 
 // 16-byte chunk swizzles (XOR on the chunk index within a row)
@@ -208,12 +214,15 @@ __device__ __forceinline__ void ring_barrier() {
 // so the loop runs up to 2 padding slices that must be emptied.  sK0..sK3 are
 // the K ring slots, sV0..sV3 the V slots; each is its own LDS array, and the
 // caller passes them in by name.
-template <int D, int MODE, bool FAST, bool PAD>
+template <int D, int MODE, bool FAST, bool PAD, int NW>
 __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile, __bf16 *sK0,
                                                __bf16 *sK1, __bf16 *sK2, __bf16 *sK3, __bf16 *sV0,
                                                __bf16 *sV1, __bf16 *sV2, __bf16 *sV3) {
     Tile tl;
     if (!decode_tile(a, MODE, tile, tl)) return;
+    constexpr int RPW = 256 / NW;       // query rows per wave
+    constexpr int NG = RPW / 32;        // 32-row column groups per wave
+    static_assert(NG >= 1 && RPW * NW == 256, "wave layout");
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave: scalar
@@ -222,14 +231,14 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     const __bf16 *__restrict__ kp = static_cast<const __bf16 *>(a.k);
     const __bf16 *__restrict__ vp = static_cast<const __bf16 *>(a.v);
     const int nh = tl.nslice;
-    const int wfirst = tl.t0 + wave * kWaveRows;   // OWN / DENSE: the wave's first row
+    const int wfirst = tl.t0 + wave * RPW;   // OWN / DENSE: the wave's first row
 
     // this lane's two query rows (column groups g = 0, 1)
-    bool rvalid[2];
-    int t[2], h[2], slot[2], tq[2];
+    bool rvalid[NG];
+    int t[NG], h[NG], slot[NG], tq[NG];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        const int r = wave * kWaveRows + g * 32 + col;
+    for (int g = 0; g < NG; ++g) {
+        const int r = wave * RPW + g * 32 + col;
         slot[g] = 0;
         if (MODE == kPast) {
             rvalid[g] = r < tl.nrows;
@@ -248,7 +257,7 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     // ---- K / V staging: global -> LDS directly, 1 KB (64 lanes x 16 B) per instruction
     constexpr int CPR = D / 8;              // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;           // rows per instruction
-    constexpr int IPS = kS / RPI / 4;       // instructions per wave per slice
+    constexpr int IPS = kS / RPI / NW;      // instructions per wave per slice
     static_assert(IPS >= 1, "slice too small for the staging pattern");
     const size_t rstride = (size_t)a.Hkv * D;
     const size_t kvoff = ((size_t)tl.b * a.S + tl.key_begin) * rstride + (size_t)tl.g * D;
@@ -289,9 +298,9 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     load_v(1, sV1);
     load_v(2, sV2);
 
-    bf16x8_t qf[2][D / 16];
+    bf16x8_t qf[NG][D / 16];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < NG; ++g) {
         if (rvalid[g]) {
             const __bf16 *src = qp + (((size_t)tl.b * a.S + t[g]) * a.Hq + h[g]) * D + half * 8;
 #pragma unroll
@@ -311,9 +320,9 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     // Tracking pass: raw q, the scale applied in fp32 at the exponent, exact for
     // logits of any size.  qn2 = |q|^2 in the same units.
     const float sl2 = a.scale_log2;
-    float qn2[2];
+    float qn2[NG];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < NG; ++g) {
         float acc = 0.f;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
@@ -343,7 +352,10 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     constexpr float kBound2 = 64.f * 64.f;
     __builtin_amdgcn_s_waitcnt(0);   // this wave's part of the first slices is in LDS
     if constexpr (FAST) {
-        if (__syncthreads_or(!(qn2[0] * kn2 <= kBound2 && qn2[1] * kn2 <= kBound2))) {
+        bool in_bound = true;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) in_bound = in_bound && qn2[g] * kn2 <= kBound2;
+        if (__syncthreads_or(!in_bound)) {
             if (threadIdx.x == 0) a.defer_list[atomicAdd(a.defer_count, 1u)] = tile;
             return;
         }
@@ -351,16 +363,21 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         __syncthreads();
     }
 
-    f32x16_t oacc[2][D / 32];
+    f32x16_t oacc[NG][D / 32];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) oacc[g][dt][i] = 0.f;
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    float m_run[NG], l_run[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        m_run[g] = -INFINITY;
+        l_run[g] = 0.f;
+    }
 
-    typedef f32x16_t HTile[2];     // S^T of one slice, per column group
+    typedef f32x16_t HTile[NG];    // S^T of one slice, per column group
     typedef bf16x8_t KRegs[D / 16];        // K operand of one slice (this lane's part)
     typedef bf16x8_t VRegs[2][D / 32];     // V^T operand of one slice (this lane's part)
     const f32x16_t zero16 = {};
@@ -377,7 +394,7 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-            for (int g = 0; g < 2; ++g)
+            for (int g = 0; g < NG; ++g)
                 sa[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kk], qf[g][kk], kk == 0 ? zero16 : sa[g],
                                                                 0, 0, 0);
     };
@@ -385,12 +402,12 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     // OWN / DENSE: causal mask on the slices that reach past the wave's first
     // row; it also empties the padding slices, whose keys all lie beyond the
     // tile's last row.  PAST: padding slices are emptied whole.
-    auto mask_max = [&](HTile &sa, int hs, float (&mx)[2], auto fast_c) {
+    auto mask_max = [&](HTile &sa, int hs, float (&mx)[NG], auto fast_c) {
         const int kb = tl.key_begin + hs * kS;
         if constexpr (MODE != kPast) {
             if (kb + kS - 1 > wfirst) {
 #pragma unroll
-                for (int g = 0; g < 2; ++g)
+                for (int g = 0; g < NG; ++g)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int key = kb + 8 * (i >> 2) + 4 * half + (i & 3);
@@ -400,14 +417,14 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         } else if constexpr (PAD) {
             if (hs >= nh) {
 #pragma unroll
-                for (int g = 0; g < 2; ++g)
+                for (int g = 0; g < NG; ++g)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) sa[g][i] = -INFINITY;
             }
         }
         if constexpr (!decltype(fast_c)::value) {
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
+            for (int g = 0; g < NG; ++g) {
                 float m = fmaxf(sa[g][0], sa[g][1]);
 #pragma unroll
                 for (int i = 2; i < 16; i += 2) m = fmaxf(m, fmaxf(sa[g][i], sa[g][i + 1]));
@@ -415,10 +432,13 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
             }
         }
     };
-    auto rescale = [&](const float (&mc)[2]) {
-        if (__any(mc[0] > m_run[0] + kRescaleSlack || mc[1] > m_run[1] + kRescaleSlack)) {
+    auto rescale = [&](const float (&mc)[NG]) {
+        bool up = false;
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < NG; ++g) up = up || mc[g] > m_run[g] + kRescaleSlack;
+        if (__any(up)) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
                 const float m_new = fmaxf(m_run[g], mc[g]);
                 const float alpha =
                     (m_run[g] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - m_new);
@@ -488,9 +508,13 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
 
     {
         const std::integral_constant<bool, FAST> fast_c;
-        if (FAST) m_run[0] = m_run[1] = 0.f;
+        if (FAST)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) m_run[g] = 0.f;
         HTile sa, sb;
-        float mxa[2] = {0.f, 0.f}, mxb[2] = {0.f, 0.f};
+        float mxa[NG], mxb[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) mxa[g] = mxb[g] = 0.f;
         KRegs kr;
         read_k(kr, sK0);
         s_mfma(sa, kr);
@@ -507,7 +531,7 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         // two steps back) have landed and every read of the slots that phase B
         // refills has completed.  The last steps compute S values that nothing
         // uses, from the clamped reloads of the last slices.
-        auto step = [&](int hs, HTile &cur, float (&mc)[2], HTile &nxt, float (&mn)[2],
+        auto step = [&](int hs, HTile &cur, float (&mc)[NG], HTile &nxt, float (&mn)[NG],
                         const __bf16 *vc, const __bf16 *kn, __bf16 *kl, __bf16 *vl) {
             // An opaque zero added to the K slot addresses keeps them inside the
             // loop, where the slot base folds into the LDS instruction's offset,
@@ -516,7 +540,7 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
             asm volatile("s_mov_b32 %0, 0" : "=s"(z));
             if constexpr (!FAST) rescale(mc);
             s_mfma(nxt, kr);
-            bf16x8_t pb[2][2];
+            bf16x8_t pb[NG][2];
             exp_group(cur, 0, pb[0], fast_c);
             VRegs vr;
             read_v(vr, vc);
@@ -525,8 +549,11 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
             load_k(hs + 4, kl);
             load_v(hs + 3, vl);
             pv_group(pb[0], vr, 0);
-            exp_group(cur, 1, pb[1], fast_c);
-            pv_group(pb[1], vr, 1);
+#pragma unroll
+            for (int g = 1; g < NG; ++g) {
+                exp_group(cur, g, pb[g], fast_c);
+                pv_group(pb[g], vr, g);
+            }
             mask_max(nxt, hs + 1, mn, fast_c);
             __builtin_amdgcn_sched_barrier(0);
         };
@@ -542,27 +569,29 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     __builtin_amdgcn_s_waitcnt(0);   // the clamped reloads have landed before LDS is reused
     __syncthreads();
 
-    float inv[2], lse[2];
+    float inv[NG], lse[NG];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < NG; ++g) {
         const float l_tot = l_run[g] + __shfl_xor(l_run[g], 32, 64);
         inv[g] = 1.f / l_tot;
         lse[g] = m_run[g] + __log2f(l_tot);
     }
     // Destination of each row: a partial slot with its log-sum-exp (past
     // blocks; the own block of a row that has past blocks to merge with), or
-    // the output row.  The normalised rows (bf16) pass through the wave's two
-    // LDS slots, column group g in slot g, chunk-swizzled, so that every global
-    // store writes whole 16-byte pieces of contiguous rows.
+    // the output row.  The normalised rows (bf16) of column group g pass
+    // through ring slot g NW + wave (of sK0..3, sV0..3), chunk-swizzled, so that
+    // every global store writes whole 16-byte pieces of contiguous rows.
     constexpr int LPR = D / 8;          // lanes per row (8 elements each)
     constexpr int RPP = 64 / LPR;       // rows per store pass
-    __bf16 *stA = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sK2 : sK3;
-    __bf16 *stB = wave == 0 ? sV0 : wave == 1 ? sV1 : wave == 2 ? sV2 : sV3;
-    const bool to_part = MODE == kPast || (MODE == kOwn && tl.npast > 0);
-    long long dst[2];                   // element offset of the row's destination, -1: padding
+    __bf16 *const ring[8] = {sK0, sK1, sK2, sK3, sV0, sV1, sV2, sV3};
+    __bf16 *stg[NG];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        __bf16 *stage = g == 0 ? stA : stB;
+    for (int g = 0; g < NG; ++g) stg[g] = ring[g * NW + wave];
+    const bool to_part = MODE == kPast || (MODE == kOwn && tl.npast > 0);
+    long long dst[NG];                  // element offset of the row's destination, -1: padding
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        __bf16 *stage = stg[g];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -587,8 +616,8 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     __syncthreads();
     __bf16 *base = static_cast<__bf16 *>(to_part ? a.part_o : a.out);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        const __bf16 *stage = g == 0 ? stA : stB;
+    for (int g = 0; g < NG; ++g) {
+        const __bf16 *stage = stg[g];
 #pragma unroll
         for (int it = 0; it < 32 / RPP; ++it) {
             const int rr = it * RPP + lane / LPR, ch = lane % LPR;
@@ -614,19 +643,19 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     __shared__ __attribute__((aligned(16))) __bf16 sV3[kS * (D)];
 
 template <int D, int MODE, bool PAD>
-__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * attn_waves<D>(), 1) void attn_bf16_kernel(AttnArgs a) {
     MOBA_RING_ARRAYS(D)
-    attn_bf16_tile<D, MODE, true, PAD>(a, xcd_tile(blockIdx.x, gridDim.x), sK0, sK1, sK2, sK3, sV0, sV1,
+    attn_bf16_tile<D, MODE, true, PAD, attn_waves<D>()>(a, xcd_tile(blockIdx.x, gridDim.x), sK0, sK1, sK2, sK3, sV0, sV1,
                                   sV2, sV3);
 }
 
 // Tracking pass: a persistent grid walks the deferred tiles (normally none).
 template <int D, int MODE, bool PAD>
-__global__ __launch_bounds__(256, 1) void attn_bf16_track_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * attn_waves<D>(), 1) void attn_bf16_track_kernel(AttnArgs a) {
     MOBA_RING_ARRAYS(D)
     const unsigned n = *a.defer_count;
     for (unsigned i = blockIdx.x; i < n; i += gridDim.x) {
-        attn_bf16_tile<D, MODE, false, PAD>(a, a.defer_list[i], sK0, sK1, sK2, sK3, sV0, sV1, sV2, sV3);
+        attn_bf16_tile<D, MODE, false, PAD, attn_waves<D>()>(a, a.defer_list[i], sK0, sK1, sK2, sK3, sV0, sV1, sV2, sV3);
         __syncthreads();
     }
 }
@@ -760,8 +789,8 @@ constexpr unsigned kTrackGrid = 256;
 // the bounded pass, then the tracking pass over the tiles it deferred
 template <int D, int MODE, bool PAD>
 static void bf16_pair(const AttnArgs &a, unsigned grid, hipStream_t st) {
-    attn_bf16_kernel<D, MODE, PAD><<<grid, 256, 0, st>>>(a);
-    attn_bf16_track_kernel<D, MODE, PAD><<<kTrackGrid, 256, 0, st>>>(a);
+    attn_bf16_kernel<D, MODE, PAD><<<grid, 64 * attn_waves<D>(), 0, st>>>(a);
+    attn_bf16_track_kernel<D, MODE, PAD><<<kTrackGrid, 64 * attn_waves<D>(), 0, st>>>(a);
 }
 
 template <int MODE>
