@@ -37,7 +37,7 @@ struct AttnArgs {
     void *part_o;
     float *part_lse;
     const uint64_t *lists, *list_off;
-    const uint32_t *tile_off;
+    const uint32_t *tile_off, *tile_list;
     const float *kmax2;    // [batch][Hkv][n] largest squared key norm per block
     int batch, S, Hq, Hkv, G, B, n, topk, nslot;
     int M;                 // query rows per tile
@@ -62,15 +62,8 @@ struct Tile {
 
 __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, Tile &tl) {
     if (mode == kPast) {
-        const long long L = a.L;
-        if (tile >= a.tile_off[L]) return false;
-        long long lo = 0, hi = L;
-        while (hi - lo > 1) {
-            const long long mid = (lo + hi) >> 1;
-            if (a.tile_off[mid] <= tile) lo = mid;
-            else hi = mid;
-        }
-        const long long lid = lo;
+        if (tile >= a.tile_off[a.L]) return false;
+        const long long lid = a.tile_list[tile];
         const int j = (int)(lid % a.n);
         tl.g = (int)((lid / a.n) % a.Hkv);
         tl.b = (int)(lid / ((long long)a.n * a.Hkv));
@@ -769,6 +762,7 @@ static AttnArgs make_args(const AttnBuffers &bf, const Problem &p) {
     a.q = bf.q; a.k = bf.k; a.v = bf.v; a.out = bf.out;
     a.part_o = bf.part_o; a.part_lse = bf.part_lse;
     a.lists = bf.lists; a.list_off = bf.list_off; a.tile_off = bf.tile_off;
+    a.tile_list = bf.tile_list;
     a.kmax2 = bf.kmax2;
     a.defer_count = bf.defer_count;
     a.defer_list = bf.defer_list;

@@ -10,6 +10,9 @@
 //             one global atomic per (workgroup, block).
 //   scan    : one workgroup; exclusive scan of the list lengths (row offsets)
 //             and of their tile counts (tile offsets); clears the cursors.
+//   tile map: the list index of every attention tile (a binary search over
+//             the tile offsets, once per tile), so the attention kernel finds
+//             its list with one load instead of a chain of dependent ones.
 //   scatter : LDS atomics give each selection a rank inside its workgroup,
 //             one global atomic per (workgroup, block) reserves a range, and
 //             each record is written to its slot of the list.
@@ -115,6 +118,21 @@ __global__ __launch_bounds__(1024) void scan_kernel(const uint32_t *__restrict__
     }
 }
 
+// grid ceil(tiles_upper / 256), 256 threads: tile_list[t] = the list whose tile range holds t.
+__global__ __launch_bounds__(256) void tile_map_kernel(const uint32_t *__restrict__ tile_off,
+                                                       uint32_t *__restrict__ tile_list, long long L,
+                                                       unsigned long long tiles_upper) {
+    const unsigned long long t = (unsigned long long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= tiles_upper || t >= tile_off[L]) return;
+    long long lo = 0, hi = L;
+    while (hi - lo > 1) {
+        const long long mid = (lo + hi) >> 1;
+        if (tile_off[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    tile_list[t] = (uint32_t)lo;
+}
+
 // grid (ceil(S / 256), Hq, batch), 256 threads.
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict__ idx,
                                                       uint32_t *__restrict__ cursor,
@@ -163,12 +181,16 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict_
 }
 
 hipError_t launch_index(const int32_t *idx, uint32_t *cnt, uint32_t *cursor, uint64_t *list_off,
-                        uint32_t *tile_off, uint64_t *lists, const Problem &p, hipStream_t st) {
+                        uint32_t *tile_off, uint32_t *tile_list, uint64_t tiles_upper,
+                        uint64_t *lists, const Problem &p, hipStream_t st) {
     const long long L = (long long)p.batch * p.Hkv * p.n;
     fill_u32_kernel<<<(unsigned)((L + 255) / 256), 256, 0, st>>>(cnt, L);
     dim3 grid((p.S + 255) / 256, p.Hq, p.batch);
     count_kernel<<<grid, 256, 0, st>>>(idx, cnt, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk);
     scan_kernel<<<1, 1024, 0, st>>>(cnt, cursor, list_off, tile_off, L, tile_rows(p));
+    if (tiles_upper > 0)
+        tile_map_kernel<<<(unsigned)((tiles_upper + 255) / 256), 256, 0, st>>>(tile_off, tile_list, L,
+                                                                              tiles_upper);
     scatter_kernel<<<grid, 256, 0, st>>>(idx, cursor, list_off, lists, p.S, p.Hq, p.Hkv, p.G, p.B,
                                          p.n, p.topk);
     return hipGetLastError();

@@ -19,7 +19,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
     size_t kbar = 0, kmax2 = 0, poolp = 0, pooln = 0, defer = 0, idx = 0, cnt = 0, cursor = 0,
-           list_off = 0, tile_off = 0, lists = 0, part_o = 0, part_lse = 0, total = 0;
+           list_off = 0, tile_off = 0, tile_list = 0, lists = 0, part_o = 0, part_lse = 0,
+           total = 0;
 };
 
 // Past selections over all rows: every row in block i keeps min(topk - 1, i) past blocks.
@@ -88,6 +89,7 @@ Layout prefill_layout(const Problem &p) {
     l.cursor = off; off += align_up(L * 4);
     l.list_off = off; off += align_up((L + 1) * 8);
     l.tile_off = off; off += align_up((L + 1) * 4);
+    l.tile_list = off; off += align_up((size_t)past_tiles_upper(p) * 4);
     l.lists = off; off += align_up((size_t)past_rows(p) * 8);
     l.part_o = off; off += align_up(rows * part_slots(p) * p.D * elem_size(p));
     l.part_lse = off; off += align_up(rows * part_slots(p) * 4);
@@ -167,10 +169,11 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
     uint32_t *cursor = reinterpret_cast<uint32_t *>(w + l.cursor);
     uint64_t *list_off = reinterpret_cast<uint64_t *>(w + l.list_off);
     uint32_t *tile_off = reinterpret_cast<uint32_t *>(w + l.tile_off);
+    uint32_t *tile_list = reinterpret_cast<uint32_t *>(w + l.tile_list);
     uint64_t *lists = reinterpret_cast<uint64_t *>(w + l.lists);
     bf.part_o = w + l.part_o;
     bf.part_lse = reinterpret_cast<float *>(w + l.part_lse);
-    bf.lists = lists; bf.list_off = list_off; bf.tile_off = tile_off;
+    bf.lists = lists; bf.list_off = list_off; bf.tile_off = tile_off; bf.tile_list = tile_list;
 
     const unsigned long long prow = past_rows(p);
     const unsigned long long tiles_upper = past_tiles_upper(p);
@@ -181,7 +184,8 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
     if ((e = launch_gate(q, kbar, idx, p, st)) != hipSuccess) return MOBA_ERR_HIP;
     if ((e = E.mark(MOBA_STAGE_INDEX)) != hipSuccess) return MOBA_ERR_HIP;
     if (prow > 0 &&
-        (e = launch_index(idx, cnt, cursor, list_off, tile_off, lists, p, st)) != hipSuccess)
+        (e = launch_index(idx, cnt, cursor, list_off, tile_off, tile_list, tiles_upper, lists, p,
+                          st)) != hipSuccess)
         return MOBA_ERR_HIP;
     if ((e = E.mark(MOBA_STAGE_ATTN_PAST)) != hipSuccess) return MOBA_ERR_HIP;
     if (prow > 0 && (e = launch_attn_past(bf, p, tiles_upper, st)) != hipSuccess)

@@ -49,7 +49,8 @@ hipError_t launch_pool(const void *k, const PoolBuffers &pb, const Problem &p, h
 hipError_t launch_gate(const void *q, const float *kbar, int32_t *idx, const Problem &p,
                        hipStream_t st);
 hipError_t launch_index(const int32_t *idx, uint32_t *cnt, uint32_t *cursor, uint64_t *list_off,
-                        uint32_t *tile_off, uint64_t *lists, const Problem &p, hipStream_t st);
+                        uint32_t *tile_off, uint32_t *tile_list, uint64_t tiles_upper,
+                        uint64_t *lists, const Problem &p, hipStream_t st);
 
 struct AttnBuffers {
     const void *q, *k, *v;
@@ -59,6 +60,7 @@ struct AttnBuffers {
     const uint64_t *lists;
     const uint64_t *list_off;
     const uint32_t *tile_off;
+    const uint32_t *tile_list;  // [past tiles] list index of each past-block tile
     const float *kmax2;     // [batch][Hkv][n] largest squared key norm per block
     unsigned *defer_count;  // deferred-tile list (tiles that need running-max tracking)
     unsigned *defer_list;
