@@ -14,9 +14,9 @@
 // bf16 inputs (gate_mfma_kernel): the scores come from the matrix cores.
 // A workgroup owns one (batch, KV head) and 32 TW consecutive tokens of all
 // G query heads of that KV head (one wave per 32 rows of one head), so every
-// chunk of 32 block means staged in LDS serves all of them.  The fp32 means
-// are split into bf16 hi + lo parts (hi = rne(x), lo = rne(x - hi)), so two
-// MFMAs per 16 dims give q.kbar with a relative error near 2^-17.  The 32x32
+// chunk of 32 block means staged in LDS serves all of them.  The means come
+// split into bf16 hi + lo parts by the pool pass (hi = rne(x), lo = rne(x -
+// hi)), so two MFMAs per 16 dims give q.kbar with a relative error near 2^-17.  The 32x32
 // result leaves each row's scores in two lanes (16 blocks each per chunk);
 // each lane keeps its own best list over ascending block indices, then the
 // two lists merge with an explicit (score, smaller index) order.
@@ -139,11 +139,37 @@ __device__ __forceinline__ void list_insert(float (&val)[KP], int (&ix)[KP], flo
     }
 }
 
+// Spread the 4 nibbles of a 16-bit value to the even nibbles of a 32-bit word.
+__device__ inline uint32_t spread_nibbles(uint32_t x) {
+    x &= 0xffffu;
+    x = (x | (x << 8)) & 0x00ff00ffu;
+    return (x | (x << 4)) & 0x0f0f0f0fu;
+}
+
+// Sorted descending value list: insert x (the smallest value falls off).
+// Slot p becomes the median of (old slot p-1, x, old slot p).
+template <int KP>
+__device__ __forceinline__ void value_insert(float (&val)[KP], float x) {
+#pragma unroll
+    for (int p = KP - 1; p > 0; --p) val[p] = __builtin_amdgcn_fmed3f(val[p - 1], x, val[p]);
+    val[0] = fmaxf(val[0], x);
+}
+
 // grid (ceil(S / (32 TW)), Hkv, batch), 64 G TW threads: wave w holds head
 // g G + w % G, tokens t0 .. t0 + 31 with t0 = 32 (blockIdx.x TW + w / G).
-template <int D, int KP>
+//
+// MASKS (n <= 256 blocks): two passes over the blocks instead of an index
+// list.  Pass 1 keeps only values (a branch-free median-of-three network) and
+// yields T, the row's npast-th best score.  Pass 2 recomputes the same scores
+// (bitwise identical: same instructions on the same data) and marks the blocks
+// with s > T and with s == T in 256-bit masks; the ties that fill the list are
+// the smallest indices, and the masks give the ascending output order for
+// free.  (Keeping pass 1's scores in registers instead halves the occupancy
+// and measured slower.)  !MASKS: each lane
+// keeps a sorted (score, index) list over ascending indices.
+template <int D, int KP, bool MASKS>
 __global__ __launch_bounds__(64 * kGateMaxWaves) void gate_mfma_kernel(
-    const __bf16 *__restrict__ q, const float *__restrict__ kbar, int32_t *__restrict__ idx, int S,
+    const __bf16 *__restrict__ q, const __bf16 *__restrict__ khl, int32_t *__restrict__ idx, int S,
     int Hq, int Hkv, int G, int B, int n, int topk, int TW) {
     constexpr int CPR = D / 8;                      // 16-byte chunks per row
     __shared__ __attribute__((aligned(16))) __bf16 khi[2][32 * D];
@@ -172,31 +198,18 @@ __global__ __launch_bounds__(64 * kGateMaxWaves) void gate_mfma_kernel(
                 for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.f;
         }
     }
-    float val[KP];
-    int ix[KP];
-#pragma unroll
-    for (int p = 0; p < KP; ++p) {
-        val[p] = (p < KP - npast) ? INFINITY : -INFINITY;
-        ix[p] = INT_MAX;
-    }
-    const float *kb = kbar + ((size_t)b * Hkv + g) * n * D;
+    const __bf16 *kb = khl + ((size_t)b * Hkv + g) * n * 2 * D;
     const f32x16_t zero16 = {};
-    for (int c = 0; c * 32 < jend; ++c) {
+    // stage the hi / lo parts of block means c*32 .. c*32+31, chunk-swizzled rows
+    auto stage = [&](int c) {
         const int buf = c & 1;
-        // stage block means c*32 .. c*32+31 as bf16 hi / lo, chunk-swizzled rows
         for (int it = tid; it < 32 * CPR; it += nthreads) {
             const int r = it / CPR, ch = it % CPR;
             const int j = c * 32 + r;
             bf16x8_t hi, lo;
             if (j < n) {
-                const float4 x0 = *reinterpret_cast<const float4 *>(kb + (size_t)j * D + ch * 8);
-                const float4 x1 = *reinterpret_cast<const float4 *>(kb + (size_t)j * D + ch * 8 + 4);
-                const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    hi[e] = (__bf16)x[e];
-                    lo[e] = (__bf16)(x[e] - (float)hi[e]);
-                }
+                hi = *reinterpret_cast<const bf16x8_t *>(kb + (size_t)j * 2 * D + ch * 8);
+                lo = *reinterpret_cast<const bf16x8_t *>(kb + (size_t)j * 2 * D + D + ch * 8);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) hi[e] = lo[e] = (__bf16)0.f;
@@ -205,93 +218,203 @@ __global__ __launch_bounds__(64 * kGateMaxWaves) void gate_mfma_kernel(
             *reinterpret_cast<bf16x8_t *>(&khi[buf][off]) = hi;
             *reinterpret_cast<bf16x8_t *>(&klo[buf][off]) = lo;
         }
-        __syncthreads();
-        if (c * 32 < own) {
-            // S^T of 32 blocks x 32 rows: rows = blocks, columns = queries
-            f32x16_t sa = zero16;
-            const int sw = col & (CPR - 1);
+    };
+    // S^T of 32 blocks x 32 rows: rows = blocks, columns = queries; lane
+    // (col, half) gets blocks c*32 + 8 (i / 4) + 4 half + i % 4 of row col
+    auto scores = [&](int c) {
+        const int buf = c & 1;
+        f32x16_t sa = zero16;
+        const int sw = col & (CPR - 1);
 #pragma unroll
-            for (int kk = 0; kk < D / 16; ++kk) {
-                const int off = col * D + (((kk * 2 + half) ^ sw) << 3);
-                const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(&khi[buf][off]);
-                const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(&klo[buf][off]);
-                sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[kk], sa, 0, 0, 0);
-                sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[kk], sa, 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int j = c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                if (j < own && sa[i] > val[KP - 1]) list_insert<KP>(val, ix, sa[i], j);
-            }
+        for (int kk = 0; kk < D / 16; ++kk) {
+            const int off = col * D + (((kk * 2 + half) ^ sw) << 3);
+            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(&khi[buf][off]);
+            const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(&klo[buf][off]);
+            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[kk], sa, 0, 0, 0);
+            sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[kk], sa, 0, 0, 0);
         }
-    }
-    // merge the partner lane's live entries: higher score first, then smaller
-    // index.  Both lanes merge at once, so the partner's list is copied whole
-    // before either list changes.
-    float pv[KP];
-    int pj[KP];
-#pragma unroll
-    for (int p = 0; p < KP; ++p) {
-        pv[p] = __shfl_xor(val[p], 32, 64);
-        pj[p] = __shfl_xor(ix[p], 32, 64);
-    }
-#pragma unroll
-    for (int p = 0; p < KP; ++p) {
-        float cs = pv[p];
-        int cj = pj[p];
-        if (p >= KP - npast) {
-#pragma unroll
-            for (int o = 0; o < KP; ++o) {
-                const bool cc = cs > val[o] || (cs == val[o] && cj < ix[o]);
-                const float tv = val[o];
-                const int ti = ix[o];
-                val[o] = cc ? cs : tv;
-                ix[o] = cc ? cj : ti;
-                cs = cc ? tv : cs;
-                cj = cc ? ti : cj;
-            }
-        }
-    }
-    if (!valid || half) return;
+        return sa;
+    };
     int32_t *dst = idx + (((size_t)b * Hq + h) * S + t) * topk;
+
+    if constexpr (MASKS) {
+        // pass 1: the npast best values of the lane's blocks, then of the row
+        float val[KP];
 #pragma unroll
-    for (int p = 0; p < KP; ++p) {
-        if (p >= KP - npast) {
-            int r = 0;
+        for (int p = 0; p < KP; ++p) val[p] = (p < KP - npast) ? INFINITY : -INFINITY;
+        for (int c = 0; c * 32 < jend; ++c) {
+            stage(c);
+            __syncthreads();
+            if (c * 32 < own) {
+                const f32x16_t sa = scores(c);
 #pragma unroll
-            for (int o = 0; o < KP; ++o) r += (o >= KP - npast && ix[o] < ix[p]) ? 1 : 0;
-            dst[r] = ix[p];
+                for (int i = 0; i < 16; ++i) {
+                    const int j = c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                    value_insert<KP>(val, j < own ? sa[i] : -INFINITY);
+                }
+            }
         }
+        float pv[KP];
+#pragma unroll
+        for (int p = 0; p < KP; ++p) pv[p] = __shfl_xor(val[p], 32, 64);
+#pragma unroll
+        for (int p = 0; p < KP; ++p)
+            if (p >= KP - npast) value_insert<KP>(val, pv[p]);
+        const float T = val[KP - 1];
+        __syncthreads();   // every wave is done with the staging buffers of pass 1
+
+        // pass 2: blocks above T and blocks equal to T, 16 bits per chunk
+        uint32_t gtm[4] = {0u, 0u, 0u, 0u}, tim[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            if (c * 32 < jend) {
+                stage(c);
+                __syncthreads();
+                if (c * 32 < own) {
+                    const f32x16_t sa = scores(c);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int j = c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                        const uint32_t bit = 1u << (16 * (c & 1) + i);
+                        if (j < own && sa[i] > T) gtm[c >> 1] |= bit;
+                        if (j < own && sa[i] == T) tim[c >> 1] |= bit;
+                    }
+                }
+            }
+        }
+        uint32_t pg[4], pt[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            pg[w] = __shfl_xor(gtm[w], 32, 64);
+            pt[w] = __shfl_xor(tim[w], 32, 64);
+        }
+        if (!valid || half) return;
+        // 256-bit masks over the blocks: chunk c is word c; this lane holds the
+        // even nibbles (blocks 8m .. 8m+3), the partner the odd ones
+        uint32_t fg[8], ft[8];
+        int ngt = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int sh = 16 * (c & 1);
+            fg[c] = spread_nibbles(gtm[c >> 1] >> sh) | (spread_nibbles(pg[c >> 1] >> sh) << 4);
+            ft[c] = spread_nibbles(tim[c >> 1] >> sh) | (spread_nibbles(pt[c >> 1] >> sh) << 4);
+            ngt += __builtin_popcount(fg[c]);
+        }
+        int need = npast - ngt;        // ties at T, smallest indices first
+        int r = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            uint32_t w = ft[c], keep = 0u;
+            while (need > 0 && w) {
+                const uint32_t low = w & (0u - w);
+                keep |= low;
+                w ^= low;
+                --need;
+            }
+            uint32_t f = fg[c] | keep;
+            while (f) {
+                if (r < npast) dst[r] = c * 32 + __builtin_ctz(f);   // npast exactly, unless a score is NaN
+                ++r;
+                f &= f - 1;
+            }
+        }
+        dst[npast] = own;
+        for (int cc = npast + 1; cc < topk; ++cc) dst[cc] = -1;
+        return;
+    } else {
+        float val[KP];
+        int ix[KP];
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+            val[p] = (p < KP - npast) ? INFINITY : -INFINITY;
+            ix[p] = INT_MAX;
+        }
+        for (int c = 0; c * 32 < jend; ++c) {
+            stage(c);
+            __syncthreads();
+            if (c * 32 < own) {
+                const f32x16_t sa = scores(c);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int j = c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                    if (j < own && sa[i] > val[KP - 1]) list_insert<KP>(val, ix, sa[i], j);
+                }
+            }
+        }
+        // merge the partner lane's live entries: higher score first, then smaller
+        // index.  Both lanes merge at once, so the partner's list is copied whole
+        // before either list changes.
+        float pv[KP];
+        int pj[KP];
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+            pv[p] = __shfl_xor(val[p], 32, 64);
+            pj[p] = __shfl_xor(ix[p], 32, 64);
+        }
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+            float cs = pv[p];
+            int cj = pj[p];
+            if (p >= KP - npast) {
+#pragma unroll
+                for (int o = 0; o < KP; ++o) {
+                    const bool cc = cs > val[o] || (cs == val[o] && cj < ix[o]);
+                    const float tv = val[o];
+                    const int ti = ix[o];
+                    val[o] = cc ? cs : tv;
+                    ix[o] = cc ? cj : ti;
+                    cs = cc ? tv : cs;
+                    cj = cc ? ti : cj;
+                }
+            }
+        }
+        if (!valid || half) return;
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+            if (p >= KP - npast) {
+                int r = 0;
+#pragma unroll
+                for (int o = 0; o < KP; ++o) r += (o >= KP - npast && ix[o] < ix[p]) ? 1 : 0;
+                dst[r] = ix[p];
+            }
+        }
+        dst[npast] = own;
+        for (int cc = npast + 1; cc < topk; ++cc) dst[cc] = -1;
     }
-    dst[npast] = own;
-    for (int cc = npast + 1; cc < topk; ++cc) dst[cc] = -1;
 }
 
 // Token chunks of 32 per workgroup: G TW waves, at most kGateMaxWaves.
 inline int gate_tw(int G) { return G >= kGateMaxWaves ? 1 : (kGateMaxWaves / G >= 2 ? 2 : 1); }
 
+// Block counts up to this use the two-pass mask selection.
+constexpr int kGateMaskBlocks = 256;
+
 template <int D, int KP>
-static hipError_t gate_mfma_impl(const void *q, const float *kbar, int32_t *idx, const Problem &p,
+static hipError_t gate_mfma_impl(const void *q, const __bf16 *khl, int32_t *idx, const Problem &p,
                                  hipStream_t st) {
     const int TW = gate_tw(p.G);
     dim3 grid((p.S + 32 * TW - 1) / (32 * TW), p.Hkv, p.batch);
-    gate_mfma_kernel<D, KP><<<grid, 64 * p.G * TW, 0, st>>>(
-        static_cast<const __bf16 *>(q), kbar, idx, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk, TW);
+    if (p.n <= kGateMaskBlocks)
+        gate_mfma_kernel<D, KP, true><<<grid, 64 * p.G * TW, 0, st>>>(
+            static_cast<const __bf16 *>(q), khl, idx, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk, TW);
+    else
+        gate_mfma_kernel<D, KP, false><<<grid, 64 * p.G * TW, 0, st>>>(
+            static_cast<const __bf16 *>(q), khl, idx, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk, TW);
     return hipGetLastError();
 }
 
 template <int D>
-static hipError_t gate_mfma_kp(const void *q, const float *kbar, int32_t *idx, const Problem &p,
+static hipError_t gate_mfma_kp(const void *q, const __bf16 *khl, int32_t *idx, const Problem &p,
                                hipStream_t st) {
     const int np = p.npast;
-    if (np <= 1) return gate_mfma_impl<D, 1>(q, kbar, idx, p, st);
-    if (np <= 2) return gate_mfma_impl<D, 2>(q, kbar, idx, p, st);
-    if (np <= 4) return gate_mfma_impl<D, 4>(q, kbar, idx, p, st);
-    if (np <= 8) return gate_mfma_impl<D, 8>(q, kbar, idx, p, st);
-    if (np <= 12) return gate_mfma_impl<D, 12>(q, kbar, idx, p, st);
-    if (np <= 16) return gate_mfma_impl<D, 16>(q, kbar, idx, p, st);
-    if (np <= 24) return gate_mfma_impl<D, 24>(q, kbar, idx, p, st);
-    return gate_mfma_impl<D, 32>(q, kbar, idx, p, st);
+    if (np <= 1) return gate_mfma_impl<D, 1>(q, khl, idx, p, st);
+    if (np <= 2) return gate_mfma_impl<D, 2>(q, khl, idx, p, st);
+    if (np <= 4) return gate_mfma_impl<D, 4>(q, khl, idx, p, st);
+    if (np <= 8) return gate_mfma_impl<D, 8>(q, khl, idx, p, st);
+    if (np <= 12) return gate_mfma_impl<D, 12>(q, khl, idx, p, st);
+    if (np <= 16) return gate_mfma_impl<D, 16>(q, khl, idx, p, st);
+    if (np <= 24) return gate_mfma_impl<D, 24>(q, khl, idx, p, st);
+    return gate_mfma_impl<D, 32>(q, khl, idx, p, st);
 }
 
 // Every causal block is selected (topk >= number of blocks): no scoring needed.
@@ -326,15 +449,15 @@ static hipError_t gate_kp(const void *q, const float *kbar, int32_t *idx, const 
     return gate_impl<T, D, 32>(q, kbar, idx, p, st);
 }
 
-hipError_t launch_gate(const void *q, const float *kbar, int32_t *idx, const Problem &p,
-                       hipStream_t st) {
+hipError_t launch_gate(const void *q, const float *kbar, const __bf16 *khl, int32_t *idx,
+                       const Problem &p, hipStream_t st) {
     if (p.dense) {
         dim3 grid((p.S + 255) / 256, p.Hq, p.batch);
         gate_all_kernel<<<grid, 256, 0, st>>>(idx, p.S, p.Hq, p.B, p.topk);
         return hipGetLastError();
     }
     if (p.dtype == kBF16 && p.G <= kGateMaxWaves)
-        return p.D == 64 ? gate_mfma_kp<64>(q, kbar, idx, p, st) : gate_mfma_kp<128>(q, kbar, idx, p, st);
+        return p.D == 64 ? gate_mfma_kp<64>(q, khl, idx, p, st) : gate_mfma_kp<128>(q, khl, idx, p, st);
     if (p.dtype == kBF16)
         return p.D == 64 ? gate_kp<__bf16, 64>(q, kbar, idx, p, st)
                          : gate_kp<__bf16, 128>(q, kbar, idx, p, st);

@@ -18,7 +18,7 @@ constexpr long long kMaxSeq = 1ll << 24;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-    size_t kbar = 0, kmax2 = 0, poolp = 0, pooln = 0, defer = 0, idx = 0, cnt = 0, cursor = 0,
+    size_t kbar = 0, kmax2 = 0, khl = 0, poolp = 0, pooln = 0, defer = 0, idx = 0, cnt = 0, cursor = 0,
            list_off = 0, tile_off = 0, tile_list = 0, lists = 0, part_o = 0, part_lse = 0,
            total = 0;
 };
@@ -65,6 +65,7 @@ Layout gate_layout(const Problem &p) {
     const size_t blocks = (size_t)p.batch * p.Hkv * p.n;
     l.kbar = off; off += align_up(blocks * p.D * 4);
     l.kmax2 = off; off += align_up(blocks * 4);
+    l.khl = off; off += align_up(blocks * 2 * p.D * 2);
     l.poolp = off; off += align_up(blocks * nchunk * p.D * 4);
     l.pooln = off; off += align_up(blocks * nchunk * 4);
     l.total = off;
@@ -112,6 +113,7 @@ PoolBuffers pool_buffers(char *w, const Layout &l, float *kbar_out) {
     PoolBuffers pb;
     pb.kbar = kbar_out ? kbar_out : reinterpret_cast<float *>(w + l.kbar);
     pb.kmax2 = reinterpret_cast<float *>(w + l.kmax2);
+    pb.khl = reinterpret_cast<__bf16 *>(w + l.khl);
     pb.partial = reinterpret_cast<float *>(w + l.poolp);
     pb.partial_nmax = reinterpret_cast<float *>(w + l.pooln);
     return pb;
@@ -181,7 +183,7 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
     if ((e = E.mark(MOBA_STAGE_POOL)) != hipSuccess) return MOBA_ERR_HIP;
     if ((e = launch_pool(k, pb, p, st)) != hipSuccess) return MOBA_ERR_HIP;
     if ((e = E.mark(MOBA_STAGE_GATE)) != hipSuccess) return MOBA_ERR_HIP;
-    if ((e = launch_gate(q, kbar, idx, p, st)) != hipSuccess) return MOBA_ERR_HIP;
+    if ((e = launch_gate(q, kbar, pb.khl, idx, p, st)) != hipSuccess) return MOBA_ERR_HIP;
     if ((e = E.mark(MOBA_STAGE_INDEX)) != hipSuccess) return MOBA_ERR_HIP;
     if (prow > 0 &&
         (e = launch_index(idx, cnt, cursor, list_off, tile_off, tile_list, tiles_upper, lists, p,
@@ -253,7 +255,7 @@ moba_status_t moba_gate(const void *q, const void *k, int32_t *block_idx, int ba
     const PoolBuffers pb = pool_buffers(w, l, nullptr);
     hipError_t e = hipSuccess;
     if (!p.dense) e = launch_pool(k, pb, p, st);
-    if (e == hipSuccess) e = launch_gate(q, pb.kbar, block_idx, p, st);
+    if (e == hipSuccess) e = launch_gate(q, pb.kbar, pb.khl, block_idx, p, st);
     return hip_status(e);
 }
 

@@ -42,12 +42,13 @@ __device__ inline uint32_t xcd_tile(uint32_t bid, uint32_t nb) {
 struct PoolBuffers {
     float *kbar;           // [batch][Hkv][n][D] block means
     float *kmax2;          // [batch][Hkv][n] largest squared key norm of each block
+    __bf16 *khl;           // [batch][Hkv][n][2][D] bf16 split of the means: hi = rne(x), lo = rne(x - hi)
     float *partial;        // [batch][Hkv][n][chunks][D] chunk sums
     float *partial_nmax;   // [batch][Hkv][n][chunks] chunk norm maxima
 };
 hipError_t launch_pool(const void *k, const PoolBuffers &pb, const Problem &p, hipStream_t st);
-hipError_t launch_gate(const void *q, const float *kbar, int32_t *idx, const Problem &p,
-                       hipStream_t st);
+hipError_t launch_gate(const void *q, const float *kbar, const __bf16 *khl, int32_t *idx,
+                       const Problem &p, hipStream_t st);
 hipError_t launch_index(const int32_t *idx, uint32_t *cnt, uint32_t *cursor, uint64_t *list_off,
                         uint32_t *tile_off, uint32_t *tile_list, uint64_t tiles_upper,
                         uint64_t *lists, const Problem &p, hipStream_t st);

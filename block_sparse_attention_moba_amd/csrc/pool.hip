@@ -7,8 +7,9 @@
 // D/8 lanes, so a wave reads 64 x 16 contiguous bytes per step) and writes
 // the chunk's fp32 column sums and the largest squared key norm of the chunk.
 // pool_finalize: sums the chunk partials of a block in a fixed order and
-// divides by the block size, and takes the block's largest squared key norm
-// (the attention kernels bound every logit of the block by it).  No atomics,
+// divides by the block size, writes the mean also as a bf16 hi + lo pair (the
+// operands of the matrix-core gate), and takes the block's largest squared key
+// norm (the attention kernels bound every logit of the block by it).  No atomics,
 // so the result is bitwise reproducible.
 #include "moba_internal.hpp"
 
@@ -90,6 +91,7 @@ __global__ __launch_bounds__(256) void pool_finalize_kernel(const float *__restr
                                                             const float *__restrict__ partial_nmax,
                                                             float *__restrict__ kbar,
                                                             float *__restrict__ kmax2,
+                                                            __bf16 *__restrict__ khl,
                                                             long long total, int D, int nchunk,
                                                             int B) {
     const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -99,7 +101,12 @@ __global__ __launch_bounds__(256) void pool_finalize_kernel(const float *__restr
     const float *src = partial + (size_t)blk * nchunk * D + i;
     float s = 0.f;
     for (int c = 0; c < nchunk; ++c) s += src[(size_t)c * D];
-    kbar[e] = s / (float)B;
+    const float m = s / (float)B;
+    kbar[e] = m;
+    // bf16 split for the matrix-core gate: m = hi + lo + O(2^-17 |m|)
+    const __bf16 hi = (__bf16)m;
+    khl[(blk * 2) * D + i] = hi;
+    khl[(blk * 2 + 1) * D + i] = (__bf16)(m - (float)hi);
     if (i == 0) {
         float m = 0.f;
         for (int c = 0; c < nchunk; ++c) m = fmaxf(m, partial_nmax[(size_t)blk * nchunk + c]);
@@ -117,7 +124,7 @@ static hipError_t pool_impl(const void *k, const PoolBuffers &pb, const Problem 
                                                     pb.partial_nmax, p.S, p.Hkv, p.B, p.n, CT);
     const long long total = (long long)p.batch * p.Hkv * p.n * D;
     pool_finalize_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(
-        pb.partial, pb.partial_nmax, pb.kbar, pb.kmax2, total, D, nchunk, p.B);
+        pb.partial, pb.partial_nmax, pb.kbar, pb.kmax2, pb.khl, total, D, nchunk, p.B);
     return hipGetLastError();
 }
 
