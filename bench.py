@@ -112,7 +112,18 @@ def time_dense(moba, torch, cfg, q, k, v):
     return e0.elapsed_time(e1)
 
 
-def cpu_baseline(cfg, host, n_rows=2048, seed=5):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(cfg, host, n_rows=8192, seed=5):
     """The fp64 oracle on the host cores: full pool, gate + attention on a
     random sample of query rows, extrapolated to the whole problem."""
     import numpy as np
@@ -138,6 +149,8 @@ def cpu_baseline(cfg, host, n_rows=2048, seed=5):
         "value": b * S / est,
         "unit": "tokens/s",
         "cores": oracle.num_threads(),
+        "host_cpus": os.cpu_count(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"full fp64 pool of K ({t1 - t0:.2f} s) + gate and attention of "
                    f"{n_rows} uniformly random query rows ({t2 - t1:.2f} s), extrapolated "
