@@ -5,8 +5,8 @@ include/moba.h); this package is its thin Python binding.
 """
 from ._lib import (MOBA_DTYPE_BF16, MOBA_DTYPE_FP32, MOBA_NUM_STAGES, STAGE_NAMES, MobaError,
                    lib, moba_abi_version, moba_gate, moba_pool, moba_prefill, moba_status_string,
-                   moba_workspace_size)
+                   moba_workspace_size, moba_workspace_size_chunked)
 
 __all__ = ["MOBA_DTYPE_BF16", "MOBA_DTYPE_FP32", "MOBA_NUM_STAGES", "STAGE_NAMES", "MobaError",
            "lib", "moba_abi_version", "moba_gate", "moba_pool", "moba_prefill",
-           "moba_status_string", "moba_workspace_size"]
+           "moba_status_string", "moba_workspace_size", "moba_workspace_size_chunked"]

@@ -23,7 +23,8 @@ MOBA_DTYPE_FP32 = 1
 MOBA_NUM_STAGES = 5
 STAGE_NAMES = ("pool", "gate", "index", "attn_past", "attn_own_merge")
 EXPORTS = ("moba_abi_version", "moba_status_string", "moba_workspace_size", "moba_pool",
-           "moba_gate", "moba_prefill", "moba_prefill_timed")
+           "moba_gate", "moba_prefill", "moba_prefill_timed", "moba_workspace_size_chunked",
+           "moba_prefill_chunked")
 
 
 class MobaError(RuntimeError):
@@ -60,6 +61,10 @@ def lib():
     L.moba_prefill_timed.restype = ci
     L.moba_prefill_timed.argtypes = [vp, vp, vp, vp] + [ci] * 8 + [vp, sz, vp,
                                                                   ctypes.POINTER(vp)]
+    L.moba_workspace_size_chunked.restype = ci
+    L.moba_workspace_size_chunked.argtypes = [ci] * 9 + [ctypes.POINTER(sz)]
+    L.moba_prefill_chunked.restype = ci
+    L.moba_prefill_chunked.argtypes = [vp, vp, vp, vp] + [ci] * 9 + [vp, sz, vp]
     _lib = L
     return L
 
@@ -111,6 +116,17 @@ def moba_workspace_size(batch, seqlen, num_q_heads, num_kv_heads, head_dim, bloc
     return pb.value, gb.value
 
 
+def moba_workspace_size_chunked(batch, seqlen, num_q_heads, num_kv_heads, head_dim, block_size,
+                                topk, query_chunk, dtype=MOBA_DTYPE_BF16):
+    """Workspace bytes of a prefill that runs in query chunks of query_chunk tokens."""
+    pb = ctypes.c_size_t(0)
+    _check(lib().moba_workspace_size_chunked(batch, seqlen, num_q_heads, num_kv_heads, head_dim,
+                                             block_size, topk, dtype, query_chunk,
+                                             ctypes.byref(pb)),
+           "moba_workspace_size_chunked")
+    return pb.value
+
+
 def _workspace(nbytes, device, workspace):
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
@@ -148,11 +164,14 @@ def moba_gate(q, k, block_size, topk, workspace=None):
     return idx
 
 
-def moba_prefill(q, k, v, block_size, topk, out=None, workspace=None, stage_events=None):
+def moba_prefill(q, k, v, block_size, topk, out=None, workspace=None, stage_events=None,
+                 query_chunk=None):
     """MoBA causal prefill forward.  q [b, S, hq, d], k/v [b, S, hkv, d] -> out like q.
 
     stage_events: optional list of MOBA_NUM_STAGES + 1 torch.cuda.Event(enable_timing=True)
-    recorded around the stages on the current stream.
+    recorded around the stages on the current stream (with query_chunk: not supported).
+    query_chunk: run the sparse stages over query chunks of this many tokens
+    (a multiple of block_size) with one chunk's scratch (moba_prefill_chunked).
     """
     _need_cuda(q, k, v)
     if not (q.dtype == k.dtype == v.dtype):
@@ -162,11 +181,24 @@ def moba_prefill(q, k, v, block_size, topk, out=None, workspace=None, stage_even
     if k.shape != (b, S, hkv, d) or v.shape != k.shape:
         raise ValueError("k and v must be [batch, seqlen, num_kv_heads, head_dim]")
     dt = _dtype_code(q)
-    pb, _ = moba_workspace_size(b, S, hq, hkv, d, block_size, topk, dt)
+    if query_chunk is None:
+        pb, _ = moba_workspace_size(b, S, hq, hkv, d, block_size, topk, dt)
+    else:
+        pb = moba_workspace_size_chunked(b, S, hq, hkv, d, block_size, topk, query_chunk, dt)
     ws = _workspace(pb, q.device, workspace)
     if out is None:
         out = torch.empty_like(q)
     _need_cuda(out)
+    if out.dtype != q.dtype or out.shape != q.shape:
+        raise ValueError("out must match q in shape and dtype")
+    if query_chunk is not None:
+        if stage_events is not None:
+            raise ValueError("stage_events are not recorded by the chunked prefill")
+        _check(lib().moba_prefill_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), b, S, hq, hkv,
+                                          d, block_size, topk, dt, query_chunk, _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream()),
+               "moba_prefill_chunked")
+        return out
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), b, S, hq, hkv, d, block_size, topk, dt,
             _ptr(ws), ws.numel(), _stream())
     if stage_events is None:

@@ -40,6 +40,7 @@ struct AttnArgs {
     const uint32_t *tile_off, *tile_list;
     const float *kmax2;    // [batch][Hkv][n] largest squared key norm per block
     int batch, S, Hq, Hkv, G, B, n, topk, nslot;
+    int r0, R;             // query chunk [r0, r0 + R): partial buffers are chunk-local
     int M;                 // query rows per tile
     long long L;           // number of lists
     unsigned ntiles;       // tiles of OWN / DENSE launches
@@ -78,10 +79,11 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, T
     if (tile >= a.ntiles) return false;
     if (mode == kOwn) {
         const int tpb = (a.B + a.M - 1) / a.M;
+        const int nr = a.R / a.B;       // blocks of the chunk
         unsigned rest = tile;
         const int tt = rest % tpb; rest /= tpb;
         const int hh = rest % a.G; rest /= a.G;
-        const int i = rest % a.n; rest /= a.n;
+        const int i = a.r0 / a.B + (int)(rest % nr); rest /= nr;
         tl.g = rest % a.Hkv;
         tl.b = rest / a.Hkv;
         tl.h = tl.g * a.G + hh;
@@ -598,7 +600,7 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         if (rvalid[g]) {
             if (to_part) {
                 const int sl = MODE == kPast ? slot[g] : a.nslot - 1;
-                const long long id = (((long long)tl.b * a.Hq + h[g]) * a.S + t[g]) * a.nslot + sl;
+                const long long id = (((long long)tl.b * a.Hq + h[g]) * a.R + (t[g] - a.r0)) * a.nslot + sl;
                 dst[g] = id * D;
                 if (half == 0) a.part_lse[id] = lse[g];
             } else {
@@ -740,7 +742,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     if (!rvalid) return;
     const float inv = 1.f / l_run;
     const float lse = m_run + log2f(l_run);
-    const long long row_id = ((long long)tl.b * a.Hq + h) * a.S + t;
+    const long long row_id = ((long long)tl.b * a.Hq + h) * a.R + (t - a.r0);   // chunk-local
     // a partial slot (past blocks; the own block of a row with past blocks) or the output row
     if (MODE == kPast || (MODE == kOwn && tl.npast > 0)) {
         const int sl = MODE == kPast ? slot : a.nslot - 1;
@@ -767,6 +769,7 @@ static AttnArgs make_args(const AttnBuffers &bf, const Problem &p) {
     a.defer_count = bf.defer_count;
     a.defer_list = bf.defer_list;
     a.batch = p.batch; a.S = p.S; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.B = p.B; a.n = p.n;
+    a.r0 = p.r0; a.R = p.R;
     a.topk = p.topk;
     a.nslot = part_slots(p);
     a.L = (long long)p.batch * p.Hkv * p.n;
@@ -819,8 +822,7 @@ hipError_t launch_attn_past(const AttnBuffers &bf, const Problem &p, uint64_t ti
 
 hipError_t launch_attn_own(const AttnBuffers &bf, const Problem &p, hipStream_t st) {
     AttnArgs a = make_args(bf, p);
-    const unsigned long long tpb = (p.B + a.M - 1) / a.M;
-    a.ntiles = (unsigned)((unsigned long long)p.batch * p.Hkv * p.n * p.G * tpb);
+    a.ntiles = (unsigned)own_tiles(p);
     return attn_launch<kOwn>(a, p, round8(a.ntiles), st);
 }
 

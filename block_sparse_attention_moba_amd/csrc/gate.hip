@@ -40,16 +40,17 @@ template <typename T, int D, int KP>
 __global__ __launch_bounds__(256) void gate_kernel(const T *__restrict__ q,
                                                    const float *__restrict__ kbar,
                                                    int32_t *__restrict__ idx, int S, int Hq,
-                                                   int Hkv, int G, int B, int n, int topk) {
+                                                   int Hkv, int G, int B, int n, int topk, int r0,
+                                                   int R) {
     __shared__ float kb[kGateJC][D];
     const int h = blockIdx.y;
     const int b = blockIdx.z;
     const int g = h / G;
-    const int t = blockIdx.x * 256 + threadIdx.x;
-    const bool valid = t < S;
+    const int t = r0 + blockIdx.x * 256 + threadIdx.x;
+    const bool valid = t < r0 + R;
     const int own = valid ? t / B : 0;
     const int npast = min(topk - 1, own);
-    const int t_last = min((int)blockIdx.x * 256 + 255, S - 1);
+    const int t_last = min(r0 + (int)blockIdx.x * 256 + 255, r0 + R - 1);
     // rows of this workgroup need past blocks j < t_last / B at most
     const int jend = (topk > 1) ? t_last / B : 0;
 
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(256) void gate_kernel(const T *__restrict__ q,
         }
     }
     if (!valid) return;
-    int32_t *dst = idx + (((size_t)b * Hq + h) * S + t) * topk;
+    int32_t *dst = idx + (((size_t)b * Hq + h) * R + (t - r0)) * topk;
     // write the live entries in ascending block order (rank by block index)
 #pragma unroll
     for (int p = 0; p < KP; ++p) {
@@ -170,7 +171,7 @@ __device__ __forceinline__ void value_insert(float (&val)[KP], float x) {
 template <int D, int KP, bool MASKS>
 __global__ __launch_bounds__(64 * kGateMaxWaves) void gate_mfma_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ khl, int32_t *__restrict__ idx, int S,
-    int Hq, int Hkv, int G, int B, int n, int topk, int TW) {
+    int Hq, int Hkv, int G, int B, int n, int topk, int TW, int r0, int R) {
     constexpr int CPR = D / 8;                      // 16-byte chunks per row
     __shared__ __attribute__((aligned(16))) __bf16 khi[2][32 * D];
     __shared__ __attribute__((aligned(16))) __bf16 klo[2][32 * D];
@@ -178,13 +179,13 @@ __global__ __launch_bounds__(64 * kGateMaxWaves) void gate_mfma_kernel(
     const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
     const int g = blockIdx.y, b = blockIdx.z;
     const int h = g * G + wave % G;
-    const int t0 = (blockIdx.x * TW + wave / G) * 32;
+    const int t0 = r0 + (blockIdx.x * TW + wave / G) * 32;
     const int t = t0 + col;
-    const bool valid = t < S;
+    const bool valid = t < r0 + R;
     // all 32 rows of the wave share one block (B is a multiple of 64)
-    const int own = min(t0, S - 1) / B;
+    const int own = min(t0, r0 + R - 1) / B;
     const int npast = min(topk - 1, own);
-    const int t_last = min((int)(blockIdx.x * TW + TW) * 32 - 1, S - 1);
+    const int t_last = min(r0 + (int)(blockIdx.x * TW + TW) * 32 - 1, r0 + R - 1);
     const int jend = (topk > 1) ? t_last / B : 0;   // past blocks any row here can use
 
     bf16x8_t qf[D / 16];
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(64 * kGateMaxWaves) void gate_mfma_kernel(
         }
         return sa;
     };
-    int32_t *dst = idx + (((size_t)b * Hq + h) * S + t) * topk;
+    int32_t *dst = idx + (((size_t)b * Hq + h) * R + (t - r0)) * topk;
 
     if constexpr (MASKS) {
         // pass 1: the npast best values of the lane's blocks, then of the row
@@ -393,13 +394,15 @@ template <int D, int KP>
 static hipError_t gate_mfma_impl(const void *q, const __bf16 *khl, int32_t *idx, const Problem &p,
                                  hipStream_t st) {
     const int TW = gate_tw(p.G);
-    dim3 grid((p.S + 32 * TW - 1) / (32 * TW), p.Hkv, p.batch);
+    dim3 grid((p.R + 32 * TW - 1) / (32 * TW), p.Hkv, p.batch);
     if (p.n <= kGateMaskBlocks)
         gate_mfma_kernel<D, KP, true><<<grid, 64 * p.G * TW, 0, st>>>(
-            static_cast<const __bf16 *>(q), khl, idx, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk, TW);
+            static_cast<const __bf16 *>(q), khl, idx, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk, TW,
+            p.r0, p.R);
     else
         gate_mfma_kernel<D, KP, false><<<grid, 64 * p.G * TW, 0, st>>>(
-            static_cast<const __bf16 *>(q), khl, idx, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk, TW);
+            static_cast<const __bf16 *>(q), khl, idx, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk, TW,
+            p.r0, p.R);
     return hipGetLastError();
 }
 
@@ -418,22 +421,22 @@ static hipError_t gate_mfma_kp(const void *q, const __bf16 *khl, int32_t *idx, c
 }
 
 // Every causal block is selected (topk >= number of blocks): no scoring needed.
-// grid (ceil(S / 256), Hq, batch), 256 threads.
-__global__ __launch_bounds__(256) void gate_all_kernel(int32_t *__restrict__ idx, int S, int Hq,
-                                                       int B, int topk) {
-    const int t = blockIdx.x * 256 + threadIdx.x;
-    if (t >= S) return;
-    const int own = t / B;
-    int32_t *dst = idx + (((size_t)blockIdx.z * Hq + blockIdx.y) * S + t) * topk;
+// grid (ceil(R / 256), Hq, batch), 256 threads.
+__global__ __launch_bounds__(256) void gate_all_kernel(int32_t *__restrict__ idx, int Hq, int B,
+                                                       int topk, int r0, int R) {
+    const int tl = blockIdx.x * 256 + threadIdx.x;
+    if (tl >= R) return;
+    const int own = (r0 + tl) / B;
+    int32_t *dst = idx + (((size_t)blockIdx.z * Hq + blockIdx.y) * R + tl) * topk;
     for (int c = 0; c < topk; ++c) dst[c] = (c <= own) ? c : -1;
 }
 
 template <typename T, int D, int KP>
 static hipError_t gate_impl(const void *q, const float *kbar, int32_t *idx, const Problem &p,
                             hipStream_t st) {
-    dim3 grid((p.S + 255) / 256, p.Hq, p.batch);
+    dim3 grid((p.R + 255) / 256, p.Hq, p.batch);
     gate_kernel<T, D, KP><<<grid, 256, 0, st>>>(static_cast<const T *>(q), kbar, idx, p.S, p.Hq,
-                                                p.Hkv, p.G, p.B, p.n, p.topk);
+                                                p.Hkv, p.G, p.B, p.n, p.topk, p.r0, p.R);
     return hipGetLastError();
 }
 
@@ -452,8 +455,8 @@ static hipError_t gate_kp(const void *q, const float *kbar, int32_t *idx, const 
 hipError_t launch_gate(const void *q, const float *kbar, const __bf16 *khl, int32_t *idx,
                        const Problem &p, hipStream_t st) {
     if (p.dense) {
-        dim3 grid((p.S + 255) / 256, p.Hq, p.batch);
-        gate_all_kernel<<<grid, 256, 0, st>>>(idx, p.S, p.Hq, p.B, p.topk);
+        dim3 grid((p.R + 255) / 256, p.Hq, p.batch);
+        gate_all_kernel<<<grid, 256, 0, st>>>(idx, p.Hq, p.B, p.topk, p.r0, p.R);
         return hipGetLastError();
     }
     if (p.dtype == kBF16 && p.G <= kGateMaxWaves)

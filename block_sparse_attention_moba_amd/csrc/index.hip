@@ -27,24 +27,26 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p,
     if (i < n) p[i] = 0u;
 }
 
-// grid (ceil(S / 256), Hq, batch), 256 threads.
+// Query rows of the chunk [r0, r0 + R); idx rows are chunk-local.
+// grid (ceil(R / 256), Hq, batch), 256 threads.
 __global__ __launch_bounds__(256) void count_kernel(const int32_t *__restrict__ idx,
-                                                    uint32_t *__restrict__ cnt, int S, int Hq,
-                                                    int Hkv, int G, int B, int n, int topk) {
+                                                    uint32_t *__restrict__ cnt, int r0, int R,
+                                                    int Hq, int Hkv, int G, int B, int n,
+                                                    int topk) {
     __shared__ uint32_t hist[kHistMax];
     const int h = blockIdx.y, b = blockIdx.z, g = h / G;
-    const int t = blockIdx.x * 256 + threadIdx.x;
-    const int jend = min((int)blockIdx.x * 256 + 255, S - 1) / B;
+    const int t = r0 + blockIdx.x * 256 + threadIdx.x;
+    const int jend = min(r0 + (int)blockIdx.x * 256 + 255, r0 + R - 1) / B;
     const bool use_lds = n <= kHistMax;
     uint32_t *gcnt = cnt + ((size_t)b * Hkv + g) * n;
     if (use_lds) {
         for (int j = threadIdx.x; j < jend; j += 256) hist[j] = 0u;
         __syncthreads();
     }
-    if (t < S) {
+    if (t < r0 + R) {
         const int own = t / B;
         const int np = min(topk - 1, own);
-        const int32_t *row = idx + (((size_t)b * Hq + h) * S + t) * topk;
+        const int32_t *row = idx + (((size_t)b * Hq + h) * R + (t - r0)) * topk;
         for (int c = 0; c < np; ++c) {
             const int j = row[c];
             if ((unsigned)j >= (unsigned)own) continue;   // never produced by the gate
@@ -133,26 +135,28 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const uint32_t *__restric
     tile_list[t] = (uint32_t)lo;
 }
 
-// grid (ceil(S / 256), Hq, batch), 256 threads.
+// grid (ceil(R / 256), Hq, batch), 256 threads.
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict__ idx,
                                                       uint32_t *__restrict__ cursor,
                                                       const uint64_t *__restrict__ list_off,
-                                                      uint64_t *__restrict__ lists, int S, int Hq,
-                                                      int Hkv, int G, int B, int n, int topk) {
+                                                      uint64_t *__restrict__ lists, int r0, int R,
+                                                      int Hq, int Hkv, int G, int B, int n,
+                                                      int topk) {
     __shared__ uint32_t hist[kHistMax];
     __shared__ uint32_t base[kHistMax];
     const int h = blockIdx.y, b = blockIdx.z, g = h / G, hh = h % G;
-    const int t = blockIdx.x * 256 + threadIdx.x;
-    const int jend = min((int)blockIdx.x * 256 + 255, S - 1) / B;
+    const int t = r0 + blockIdx.x * 256 + threadIdx.x;
+    const bool in = t < r0 + R;
+    const int jend = min(r0 + (int)blockIdx.x * 256 + 255, r0 + R - 1) / B;
     const bool use_lds = n <= kHistMax;
     const size_t lbase = ((size_t)b * Hkv + g) * n;
     if (use_lds) {
         for (int j = threadIdx.x; j < jend; j += 256) hist[j] = 0u;
         __syncthreads();
     }
-    const int own = (t < S) ? t / B : 0;
-    const int np = (t < S) ? min(topk - 1, own) : 0;
-    const int32_t *row = idx + (((size_t)b * Hq + h) * S + (t < S ? t : 0)) * topk;
+    const int own = in ? t / B : 0;
+    const int np = in ? min(topk - 1, own) : 0;
+    const int32_t *row = idx + (((size_t)b * Hq + h) * R + (in ? t - r0 : 0)) * topk;
     uint32_t rank[kMaxPast];
 #pragma unroll
     for (int c = 0; c < kMaxPast; ++c) {
@@ -185,14 +189,14 @@ hipError_t launch_index(const int32_t *idx, uint32_t *cnt, uint32_t *cursor, uin
                         uint64_t *lists, const Problem &p, hipStream_t st) {
     const long long L = (long long)p.batch * p.Hkv * p.n;
     fill_u32_kernel<<<(unsigned)((L + 255) / 256), 256, 0, st>>>(cnt, L);
-    dim3 grid((p.S + 255) / 256, p.Hq, p.batch);
-    count_kernel<<<grid, 256, 0, st>>>(idx, cnt, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk);
+    dim3 grid((p.R + 255) / 256, p.Hq, p.batch);
+    count_kernel<<<grid, 256, 0, st>>>(idx, cnt, p.r0, p.R, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk);
     scan_kernel<<<1, 1024, 0, st>>>(cnt, cursor, list_off, tile_off, L, tile_rows(p));
     if (tiles_upper > 0)
         tile_map_kernel<<<(unsigned)((tiles_upper + 255) / 256), 256, 0, st>>>(tile_off, tile_list, L,
                                                                               tiles_upper);
-    scatter_kernel<<<grid, 256, 0, st>>>(idx, cursor, list_off, lists, p.S, p.Hq, p.Hkv, p.G, p.B,
-                                         p.n, p.topk);
+    scatter_kernel<<<grid, 256, 0, st>>>(idx, cursor, list_off, lists, p.r0, p.R, p.Hq, p.Hkv,
+                                         p.G, p.B, p.n, p.topk);
     return hipGetLastError();
 }
 

@@ -46,19 +46,21 @@ __device__ inline void store8(float *p, const float *f) {
     *reinterpret_cast<float4 *>(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
 }
 
-// grid ceil(rows / (256 / (D / 8))), 256 threads; rows ordered (batch, head, token)
+// grid ceil(rows / (256 / (D / 8))), 256 threads; rows ordered (batch, head,
+// token of the chunk [r0, r0 + R)), partial buffers chunk-local.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const T *__restrict__ part_o,
                                                     const float *__restrict__ part_lse,
                                                     T *__restrict__ out, int S, int Hq, int B,
-                                                    int topk, int nslot, long long rows) {
+                                                    int topk, int nslot, long long rows, int r0,
+                                                    int R) {
     constexpr int LPR = D / 8;
     constexpr int RPW = 256 / LPR;
     const long long row = (long long)blockIdx.x * RPW + threadIdx.x / LPR;
     const int ch = threadIdx.x % LPR;
     if (row >= rows) return;
-    const int t = (int)(row % S);
-    const long long bh = row / S;
+    const int t = r0 + (int)(row % R);
+    const long long bh = row / R;
     const int h = (int)(bh % Hq), b = (int)(bh / Hq);
     const int npast = min(topk - 1, t / B);
     if (npast == 0) return;
@@ -90,10 +92,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const T *__restrict__ part_o
 template <typename T, int D>
 hipError_t merge_impl(const AttnBuffers &bf, const Problem &p, hipStream_t st) {
     constexpr int RPW = 256 / (D / 8);
-    const long long rows = (long long)p.batch * p.Hq * p.S;
+    const long long rows = (long long)p.batch * p.Hq * p.R;
     merge_kernel<T, D><<<(unsigned)((rows + RPW - 1) / RPW), 256, 0, st>>>(
         static_cast<const T *>(bf.part_o), bf.part_lse, static_cast<T *>(bf.out), p.S, p.Hq, p.B,
-        p.topk, part_slots(p), rows);
+        p.topk, part_slots(p), rows, p.r0, p.R);
     return hipGetLastError();
 }
 

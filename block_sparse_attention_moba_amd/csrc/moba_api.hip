@@ -23,20 +23,22 @@ struct Layout {
            total = 0;
 };
 
-// Past selections over all rows: every row in block i keeps min(topk - 1, i) past blocks.
+// Past selections over the rows of the chunk: every row in block i keeps
+// min(topk - 1, i) past blocks.
 unsigned long long past_rows(const Problem &p) {
     unsigned long long per_seq = 0;
-    for (int i = 0; i < p.n; ++i) per_seq += (unsigned long long)min(p.topk - 1, i);
+    for (int i = p.r0 / p.B; i < (p.r0 + p.R) / p.B; ++i) per_seq += (unsigned long long)min(p.topk - 1, i);
     return per_seq * (unsigned long long)p.B * p.Hq * p.batch;
 }
 
 size_t elem_size(const Problem &p) { return p.dtype == kBF16 ? 2 : 4; }
 
-// Upper bound on the past-block attention tiles: every list may end in a partial tile.
-unsigned long long past_tiles_upper(const Problem &p) {
+// Upper bound on the past-block attention tiles for prow past selections:
+// every list may end in a partial tile.
+unsigned long long past_tiles_upper(const Problem &p, unsigned long long prow) {
     const unsigned long long M = (unsigned long long)tile_rows(p);
     const unsigned long long L = (unsigned long long)p.batch * p.Hkv * p.n;
-    return (past_rows(p) + M - 1) / M + L;
+    return (prow + M - 1) / M + L;
 }
 
 moba_status_t make_problem(int batch, int S, int Hq, int Hkv, int D, int B, int topk,
@@ -54,8 +56,35 @@ moba_status_t make_problem(int batch, int S, int Hq, int Hkv, int D, int B, int 
     p->n = S / B;
     p->dense = topk >= p->n;
     p->npast = min(topk - 1, p->n - 1);
+    p->r0 = 0;
+    p->R = S;
     if (!p->dense && p->npast > kMaxPast) return MOBA_ERR_UNSUPPORTED;
     return MOBA_OK;
+}
+
+// Query chunk length in tokens for a requested chunk (<= 0 or >= S: one chunk).
+int chunk_len(const Problem &p, int query_chunk) {
+    return (query_chunk <= 0 || query_chunk >= p.S) ? p.S : query_chunk;
+}
+
+// The longest chunk's rows and the most past selections of any chunk: these
+// size every chunk-local buffer.
+struct ChunkBound {
+    Problem rows;                 // r0 = 0, R = the longest chunk
+    unsigned long long prow;      // past selections of the busiest chunk
+};
+
+ChunkBound chunk_bound(const Problem &p, int C) {
+    ChunkBound cb{p, 0ull};
+    cb.rows.r0 = 0;
+    cb.rows.R = min(C, p.S);
+    Problem w = p;
+    for (int r0 = 0; r0 < p.S; r0 += C) {
+        w.r0 = r0;
+        w.R = min(C, p.S - r0);
+        cb.prow = std::max(cb.prow, past_rows(w));
+    }
+    return cb;
 }
 
 Layout gate_layout(const Problem &p) {
@@ -72,26 +101,30 @@ Layout gate_layout(const Problem &p) {
     return l;
 }
 
-Layout prefill_layout(const Problem &p) {
+// Workspace of a prefill that runs its sparse stages in query chunks of C
+// tokens (C = S: one pass); row-indexed buffers are sized for one chunk.
+Layout prefill_layout(const Problem &full, int C) {
+    const ChunkBound cb = chunk_bound(full, full.dense ? full.S : C);
+    const Problem &p = cb.rows;
     Layout l = gate_layout(p);      // block means and key-norm bounds
     size_t off = l.total;
     // deferred-tile list: a counter then one entry per tile of the largest launch
     const unsigned long long tiles =
-        p.dense ? dense_tiles(p) : std::max(past_tiles_upper(p), own_tiles(p));
+        p.dense ? dense_tiles(p) : std::max(past_tiles_upper(p, cb.prow), own_tiles(p));
     l.defer = off; off += align_up(256 + (size_t)tiles * 4);
     if (p.dense) {                  // full causal attention needs nothing more
         l.total = off;
         return l;
     }
-    const size_t rows = (size_t)p.batch * p.Hq * p.S;
+    const size_t rows = (size_t)p.batch * p.Hq * p.R;
     const size_t L = (size_t)p.batch * p.Hkv * p.n;
     l.idx = off; off += align_up(rows * p.topk * 4);
     l.cnt = off; off += align_up(L * 4);
     l.cursor = off; off += align_up(L * 4);
     l.list_off = off; off += align_up((L + 1) * 8);
     l.tile_off = off; off += align_up((L + 1) * 4);
-    l.tile_list = off; off += align_up((size_t)past_tiles_upper(p) * 4);
-    l.lists = off; off += align_up((size_t)past_rows(p) * 8);
+    l.tile_list = off; off += align_up((size_t)past_tiles_upper(p, cb.prow) * 4);
+    l.lists = off; off += align_up((size_t)cb.prow * 8);
     l.part_o = off; off += align_up(rows * part_slots(p) * p.D * elem_size(p));
     l.part_lse = off; off += align_up(rows * part_slots(p) * 4);
     l.total = off;
@@ -129,10 +162,13 @@ struct Events {
 
 moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *out, int batch,
                            int S, int Hq, int Hkv, int D, int B, int topk, moba_dtype_t dt,
-                           void *ws, size_t ws_bytes, void *stream, void *const *events) {
+                           int query_chunk, void *ws, size_t ws_bytes, void *stream,
+                           void *const *events) {
     Problem p;
     moba_status_t rc = make_problem(batch, S, Hq, Hkv, D, B, topk, dt, &p);
     if (rc != MOBA_OK) return rc;
+    if (query_chunk % B != 0) return MOBA_ERR_UNSUPPORTED;
+    const int C = chunk_len(p, query_chunk);
     if (!q || !k || !v || !out) return MOBA_ERR_INVALID_ARGUMENT;
     const size_t qbytes = (size_t)batch * S * Hq * D * elem_size(p);
     const size_t kvbytes = (size_t)batch * S * Hkv * D * elem_size(p);
@@ -141,7 +177,7 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
         return MOBA_ERR_INVALID_ARGUMENT;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
         return MOBA_ERR_UNSUPPORTED;
-    const Layout l = prefill_layout(p);
+    const Layout l = prefill_layout(p, C);
     if (ws_bytes < l.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
     if (!ws) return MOBA_ERR_INVALID_ARGUMENT;
     if (!aligned(ws, kAlign)) return MOBA_ERR_UNSUPPORTED;
@@ -177,24 +213,28 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
     bf.part_lse = reinterpret_cast<float *>(w + l.part_lse);
     bf.lists = lists; bf.list_off = list_off; bf.tile_off = tile_off; bf.tile_list = tile_list;
 
-    const unsigned long long prow = past_rows(p);
-    const unsigned long long tiles_upper = past_tiles_upper(p);
-
     if ((e = E.mark(MOBA_STAGE_POOL)) != hipSuccess) return MOBA_ERR_HIP;
     if ((e = launch_pool(k, pb, p, st)) != hipSuccess) return MOBA_ERR_HIP;
-    if ((e = E.mark(MOBA_STAGE_GATE)) != hipSuccess) return MOBA_ERR_HIP;
-    if ((e = launch_gate(q, kbar, pb.khl, idx, p, st)) != hipSuccess) return MOBA_ERR_HIP;
-    if ((e = E.mark(MOBA_STAGE_INDEX)) != hipSuccess) return MOBA_ERR_HIP;
-    if (prow > 0 &&
-        (e = launch_index(idx, cnt, cursor, list_off, tile_off, tile_list, tiles_upper, lists, p,
-                          st)) != hipSuccess)
-        return MOBA_ERR_HIP;
-    if ((e = E.mark(MOBA_STAGE_ATTN_PAST)) != hipSuccess) return MOBA_ERR_HIP;
-    if (prow > 0 && (e = launch_attn_past(bf, p, tiles_upper, st)) != hipSuccess)
-        return MOBA_ERR_HIP;
-    if ((e = E.mark(MOBA_STAGE_ATTN_OWN)) != hipSuccess) return MOBA_ERR_HIP;
-    if ((e = launch_attn_own(bf, p, st)) != hipSuccess) return MOBA_ERR_HIP;
-    if (prow > 0 && (e = launch_merge(bf, p, st)) != hipSuccess) return MOBA_ERR_HIP;
+    // the sparse stages, one query chunk at a time (stage events: last chunk)
+    for (int r0 = 0; r0 < S; r0 += C) {
+        p.r0 = r0;
+        p.R = min(C, S - r0);
+        const unsigned long long prow = past_rows(p);
+        const unsigned long long tiles_upper = past_tiles_upper(p, prow);
+        if ((e = E.mark(MOBA_STAGE_GATE)) != hipSuccess) return MOBA_ERR_HIP;
+        if ((e = launch_gate(q, kbar, pb.khl, idx, p, st)) != hipSuccess) return MOBA_ERR_HIP;
+        if ((e = E.mark(MOBA_STAGE_INDEX)) != hipSuccess) return MOBA_ERR_HIP;
+        if (prow > 0 &&
+            (e = launch_index(idx, cnt, cursor, list_off, tile_off, tile_list, tiles_upper, lists,
+                              p, st)) != hipSuccess)
+            return MOBA_ERR_HIP;
+        if ((e = E.mark(MOBA_STAGE_ATTN_PAST)) != hipSuccess) return MOBA_ERR_HIP;
+        if (prow > 0 && (e = launch_attn_past(bf, p, tiles_upper, st)) != hipSuccess)
+            return MOBA_ERR_HIP;
+        if ((e = E.mark(MOBA_STAGE_ATTN_OWN)) != hipSuccess) return MOBA_ERR_HIP;
+        if ((e = launch_attn_own(bf, p, st)) != hipSuccess) return MOBA_ERR_HIP;
+        if (prow > 0 && (e = launch_merge(bf, p, st)) != hipSuccess) return MOBA_ERR_HIP;
+    }
     if ((e = E.mark(MOBA_NUM_STAGES)) != hipSuccess) return MOBA_ERR_HIP;
     return MOBA_OK;
 }
@@ -221,8 +261,21 @@ moba_status_t moba_workspace_size(int batch, int S, int Hq, int Hkv, int D, int 
     Problem p;
     const moba_status_t rc = make_problem(batch, S, Hq, Hkv, D, B, topk, dt, &p);
     if (rc != MOBA_OK) return rc;
-    if (prefill_bytes) *prefill_bytes = prefill_layout(p).total;
+    if (prefill_bytes) *prefill_bytes = prefill_layout(p, p.S).total;
     if (gate_bytes) *gate_bytes = gate_layout(p).total;
+    return MOBA_OK;
+}
+
+moba_status_t moba_workspace_size_chunked(int batch, int S, int Hq, int Hkv, int D, int B,
+                                          int topk, moba_dtype_t dt, int query_chunk,
+                                          size_t *prefill_bytes) {
+    Problem p;
+    const moba_status_t rc = make_problem(batch, S, Hq, Hkv, D, B, topk, dt, &p);
+    if (rc != MOBA_OK) return rc;
+    if (query_chunk <= 0) return MOBA_ERR_INVALID_ARGUMENT;
+    if (query_chunk % B != 0) return MOBA_ERR_UNSUPPORTED;
+    if (!prefill_bytes) return MOBA_ERR_INVALID_ARGUMENT;
+    *prefill_bytes = prefill_layout(p, chunk_len(p, query_chunk)).total;
     return MOBA_OK;
 }
 
@@ -262,8 +315,17 @@ moba_status_t moba_gate(const void *q, const void *k, int32_t *block_idx, int ba
 moba_status_t moba_prefill(const void *q, const void *k, const void *v, void *out, int batch,
                            int S, int Hq, int Hkv, int D, int B, int topk, moba_dtype_t dt,
                            void *ws, size_t ws_bytes, void *stream) {
-    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, ws, ws_bytes, stream,
+    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, S, ws, ws_bytes, stream,
                         nullptr);
+}
+
+moba_status_t moba_prefill_chunked(const void *q, const void *k, const void *v, void *out,
+                                   int batch, int S, int Hq, int Hkv, int D, int B, int topk,
+                                   moba_dtype_t dt, int query_chunk, void *ws, size_t ws_bytes,
+                                   void *stream) {
+    if (query_chunk <= 0) return MOBA_ERR_INVALID_ARGUMENT;
+    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, query_chunk, ws,
+                        ws_bytes, stream, nullptr);
 }
 
 moba_status_t moba_prefill_timed(const void *q, const void *k, const void *v, void *out,
@@ -273,7 +335,7 @@ moba_status_t moba_prefill_timed(const void *q, const void *k, const void *v, vo
     if (!stage_events) return MOBA_ERR_INVALID_ARGUMENT;
     for (int i = 0; i <= MOBA_NUM_STAGES; ++i)
         if (!stage_events[i]) return MOBA_ERR_INVALID_ARGUMENT;
-    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, ws, ws_bytes, stream,
+    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, S, ws, ws_bytes, stream,
                         stage_events);
 }
 

@@ -30,6 +30,10 @@ struct Problem {
     int n;       // S / B
     int npast;   // topk - 1 capped at n - 1
     bool dense;  // topk >= n: plain causal attention
+    // query rows handled by one pass of the sparse stages: tokens [r0, r0 + R),
+    // both multiples of B (r0 = 0, R = S unless the prefill runs in chunks).
+    // Row-indexed scratch (block indices, lists, partial outputs) is chunk-local.
+    int r0, R;
 };
 
 // Map a workgroup index to a tile so that consecutive tiles run on the same
@@ -78,7 +82,8 @@ inline int tile_rows(const Problem &p) { return p.dtype == kBF16 ? 256 : 128; }
 
 // Tiles of each attention launch (the past-block count is an upper bound).
 inline unsigned long long own_tiles(const Problem &p) {
-    return (unsigned long long)p.batch * p.Hkv * p.n * p.G * ((p.B + tile_rows(p) - 1) / tile_rows(p));
+    return (unsigned long long)p.batch * p.Hkv * (p.R / p.B) * p.G *
+           ((p.B + tile_rows(p) - 1) / tile_rows(p));
 }
 inline unsigned long long dense_tiles(const Problem &p) {
     return (unsigned long long)p.batch * p.Hq * ((p.S + tile_rows(p) - 1) / tile_rows(p));

@@ -114,8 +114,11 @@ moba_status_t moba_pool(const void *k, float *kbar, int batch, int seqlen, int n
 /*
  * Gate and causal top-k (write-up, the first implementation step: assign
  * query tokens to KV blocks from the gate and the causal mask).  Writes
- * block_idx as laid out above.  Gate scores are fp32 inner products of the
- * query with the fp32 block means.  Workspace: at least *gate_bytes.
+ * block_idx as laid out above.  Gate scores: fp32 inputs, fp32 inner products
+ * of the query with the fp32 block means; bf16 inputs, the query against the
+ * block means split into bf16 hi + lo parts on the matrix cores with fp32
+ * accumulation (within about 2^-17 relative of the fp32 product).  Workspace:
+ * at least *gate_bytes.
  */
 moba_status_t moba_gate(const void *q, const void *k, int32_t *block_idx, int batch, int seqlen,
                         int num_q_heads, int num_kv_heads, int head_dim, int block_size,
@@ -149,6 +152,28 @@ moba_status_t moba_prefill_timed(const void *q, const void *k, const void *v, vo
                                  int head_dim, int block_size, int topk, moba_dtype_t dtype,
                                  void *workspace, size_t workspace_bytes, void *stream,
                                  void *const *stage_events);
+
+/*
+ * moba_prefill for sequences whose whole-sequence scratch does not fit: the
+ * pool runs once, then the gate, index build, past-block attention, own-block
+ * attention and merge run for the query tokens [c, c + query_chunk) of one
+ * chunk at a time, reusing one chunk's scratch (the write-up's largest
+ * context, 10M tokens, needs about 1 TB of partial outputs in one pass).  The
+ * output is the same as moba_prefill's, bit for bit.  query_chunk: tokens per
+ * chunk, a positive multiple of block_size (>= seqlen: one chunk).  Full
+ * causal attention (topk >= seqlen / block_size) needs no chunking and
+ * ignores it.  Errors as moba_prefill, plus INVALID_ARGUMENT for
+ * query_chunk <= 0 and UNSUPPORTED for query_chunk % block_size != 0.
+ */
+moba_status_t moba_workspace_size_chunked(int batch, int seqlen, int num_q_heads,
+                                          int num_kv_heads, int head_dim, int block_size,
+                                          int topk, moba_dtype_t dtype, int query_chunk,
+                                          size_t *prefill_bytes);
+moba_status_t moba_prefill_chunked(const void *q, const void *k, const void *v, void *out,
+                                   int batch, int seqlen, int num_q_heads, int num_kv_heads,
+                                   int head_dim, int block_size, int topk, moba_dtype_t dtype,
+                                   int query_chunk, void *workspace, size_t workspace_bytes,
+                                   void *stream);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,11 @@ notes):
     after p, independently with probability ``shift_prob``, ``q += u_p``.
   * Finally the tensors are rounded to the storage dtype (bf16 by
     round-to-nearest-even via torch's cast) or kept fp32.
+  * Workloads with ``gen_slice`` > 0 (10M tokens) follow the same recipe one
+    token slice [s*T, (s+1)*T) at a time: each slice draws its Q, K, V and
+    shift masks from its own torch generator seeded ``seed * 65536 + s``, the
+    planted blocks and directions come from the same NumPy draws as above, and
+    each slice is rounded into the preallocated storage-dtype tensors.
 
 Layouts are BSHD: q is [batch, S, Hq, d]; k and v are [batch, S, Hkv, d].
 """
@@ -30,6 +35,8 @@ def make_inputs(cfg: Config, device="cpu", seed=None):
     copied back to the host when the oracle needs them.
     """
     seed = cfg.seed if seed is None else seed
+    if cfg.gen_slice > 0:
+        return _make_sliced(cfg, torch.device(device), seed)
     dev = torch.device(device)
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
@@ -68,6 +75,71 @@ def make_inputs(cfg: Config, device="cpu", seed=None):
     elif cfg.dtype != "fp32":
         raise ValueError(cfg.dtype)
     return {"q": q.contiguous(), "k": k.contiguous(), "v": v.contiguous(), "planted": planted}
+
+
+def _plant_plan(cfg: Config, rng, P):
+    """Planted block ids [batch, hkv, P] and their unit directions, NumPy draws
+    in the order of the unsliced recipe."""
+    n, d = cfg.n_blocks, cfg.head_dim
+    planted = np.zeros((cfg.batch, cfg.hkv, P), dtype=np.int64)
+    dirs = {}
+    for b in range(cfg.batch):
+        for gk in range(cfg.hkv):
+            blocks = np.sort(rng.choice(n - 1, size=P, replace=False)) if P > 0 else []
+            planted[b, gk, :] = blocks
+            for p in blocks:
+                u = rng.standard_normal(d)
+                dirs[(b, gk, int(p))] = u / np.linalg.norm(u)
+    return planted, dirs
+
+
+def _make_sliced(cfg: Config, dev, seed):
+    bsz, S, hq, hkv, d = cfg.batch, cfg.seqlen, cfg.hq, cfg.hkv, cfg.head_dim
+    B, T, G = cfg.block_size, cfg.gen_slice, hq // hkv
+    inv = 1.0 / math.sqrt(d)
+    if cfg.dtype == "bf16":
+        dt = torch.bfloat16
+    elif cfg.dtype == "fp32":
+        dt = torch.float32
+    else:
+        raise ValueError(cfg.dtype)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    P = min(cfg.planted, max(cfg.n_blocks - 1, 0))
+    planted, dirs = _plant_plan(cfg, rng, P)
+    units = {key: torch.tensor(u, dtype=torch.float32, device=dev) for key, u in dirs.items()}
+    q = torch.empty((bsz, S, hq, d), dtype=dt, device=dev)
+    k = torch.empty((bsz, S, hkv, d), dtype=dt, device=dev)
+    v = torch.empty((bsz, S, hkv, d), dtype=dt, device=dev)
+    for s, t0 in enumerate(range(0, S, T)):
+        t1 = min(S, t0 + T)
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed * 65536 + s)
+        qs = torch.randn((bsz, t1 - t0, hq, d), generator=g, device=dev,
+                         dtype=torch.float32).mul_(inv)
+        ks = torch.randn((bsz, t1 - t0, hkv, d), generator=g, device=dev,
+                         dtype=torch.float32).mul_(inv)
+        vs = torch.randn((bsz, t1 - t0, hkv, d), generator=g, device=dev,
+                         dtype=torch.float32).mul_(inv)
+        for b in range(bsz):
+            for gk in range(hkv):
+                for p in planted[b, gk, :].tolist():
+                    ut = units[(b, gk, p)]
+                    k0, k1 = max(p * B, t0), min((p + 1) * B, t1)
+                    if k0 < k1:
+                        ks[b, k0 - t0:k1 - t0, gk, :] += 2.0 * ut
+                    start = max((p + 1) * B, t0)
+                    if start >= t1:
+                        continue
+                    for hh in range(G):
+                        h = gk * G + hh
+                        m = torch.rand((t1 - start,), generator=g, device=dev) < cfg.shift_prob
+                        qs[b, start - t0:, h, :].addcmul_(m.to(torch.float32)[:, None],
+                                                          ut[None, :])
+        q[:, t0:t1].copy_(qs)
+        k[:, t0:t1].copy_(ks)
+        v[:, t0:t1].copy_(vs)
+        del qs, ks, vs
+    return {"q": q, "k": k, "v": v, "planted": planted}
 
 
 def to_oracle_array(t: torch.Tensor):

@@ -75,6 +75,37 @@ def test_workspace_sizes():
     assert rc == 0 and 50e9 < pb < 200e9
 
 
+def ws_chunked(*args):
+    pb = ctypes.c_size_t(0)
+    rc = moba.lib().moba_workspace_size_chunked(*args, ctypes.byref(pb))
+    return rc, pb.value
+
+
+def test_chunked_workspace():
+    dims = (1, 1 << 20, 32, 8, 128, 4096, 12, BF16)
+    _, whole, _ = ws_size(*dims)
+    assert ws_chunked(*dims, 1 << 20) == (0, whole)          # one chunk: same scratch
+    assert ws_chunked(*dims, 1 << 22) == (0, whole)
+    rc, quarter = ws_chunked(*dims, 1 << 18)
+    assert rc == 0 and whole / 5 < quarter < whole / 3
+    rc, one_block = ws_chunked(*dims, 4096)
+    assert rc == 0 and one_block < quarter / 32
+    # 10M tokens: whole-sequence scratch is near 1 TB, 256K-token chunks fit one GPU
+    ten = (1, 10 * (1 << 20), 32, 8, 128, 4096, 12, BF16)
+    rc, big, _ = ws_size(*ten)
+    assert rc == 0 and big > 900e9
+    rc, small = ws_chunked(*ten, 1 << 18)
+    assert rc == 0 and small < 30e9
+    # a tail chunk shorter than the rest is covered
+    rc, tail = ws_chunked(1, 1920, 2, 1, 128, 192, 3, BF16, 3 * 192)
+    assert rc == 0 and tail > 0
+    assert ws_chunked(*dims, 0)[0] == INV
+    assert ws_chunked(*dims, -4096)[0] == INV
+    assert ws_chunked(*dims, 4096 + 64)[0] == UNS
+    assert ws_chunked(1, 1000, 2, 2, 64, 128, 3, BF16, 128)[0] == UNS
+    assert moba.lib().moba_workspace_size_chunked(*dims, 4096, None) == INV
+
+
 FAKE = 1 << 40          # aligned, never dereferenced: every call below fails validation
 
 
@@ -93,6 +124,19 @@ def test_prefill_rejects_before_any_hip_call():
     assert prefill(nbytes=16) == WS
     assert prefill(ws=0) == INV
     assert prefill(ws=FAKE + (4 << 32) + 16) == UNS          # workspace alignment
+
+
+def test_chunked_prefill_rejects_before_any_hip_call():
+    vp = ctypes.c_void_p
+
+    def call(chunk, nbytes=1 << 40, dims=(1, 1024, 2, 2, 64, 128, 3, BF16)):
+        return moba.lib().moba_prefill_chunked(vp(FAKE), vp(FAKE + (1 << 32)),
+                                               vp(FAKE + (2 << 32)), vp(FAKE + (3 << 32)), *dims,
+                                               chunk, vp(FAKE + (4 << 32)), nbytes, None)
+    assert call(0) == INV
+    assert call(100) == UNS
+    assert call(256, nbytes=1024) == WS
+    assert call(256, dims=(1, 1024, 2, 2, 80, 128, 3, BF16)) == UNS
 
 
 def test_timed_prefill_needs_events():

@@ -99,6 +99,9 @@ EDGE = [
           planted=6),
     small("fp32-d64-topk1", hq=2, hkv=2, seqlen=512, head_dim=64, dtype="fp32", block_size=64,
           topk=1),
+    # more than 256 blocks: the gate keeps running top-k lists instead of block masks
+    small("320-blocks-list-gate", hq=4, hkv=1, seqlen=64 * 320, head_dim=128, block_size=64,
+          topk=12, planted=12),
 ]
 
 
@@ -122,6 +125,37 @@ def test_pool_matches_oracle(dev):
         err = np.abs(kbar - ref).max() / np.abs(ref).max()
         log(f"[pool {cfg.name}] max rel err {err:.3e}")
         assert err < 1e-6
+
+
+CHUNKED = [
+    (CONFIGS[1], 1024),       # 8 chunks of 2 blocks, batch 2
+    (EDGE[0], 64),            # one block per chunk, GQA, d=64
+    (EDGE[1], 3 * 192),       # 3-block chunks and a 1-block tail, block 192
+    (EDGE[4], 256),           # fp32
+    (EDGE[5], 7 * 64),        # top-32 over 64 blocks, ragged tail chunk
+    (EDGE[7], 96 * 64),       # list gate
+]
+
+
+@pytest.mark.parametrize("cfg,chunk", CHUNKED, ids=lambda c: getattr(c, "name", str(c)))
+def test_chunked_prefill_matches_one_pass(cfg, chunk, dev):
+    """Query-chunked scratch reuse gives the one-pass output bit for bit."""
+    moba = _moba()
+    log(f"case {cfg.name} chunk={chunk} dims={dims(cfg)}")
+    inp = make_inputs(cfg)
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    one = moba.moba_prefill(q, k, v, cfg.block_size, cfg.topk)
+    ws = moba.moba_workspace_size_chunked(*dims(cfg), chunk,
+                                          0 if cfg.dtype == "bf16" else 1)
+    # a dirty workspace: every chunk must clear what it reads
+    junk = torch.full((ws,), 0x7f, dtype=torch.uint8, device=dev)
+    part = moba.moba_prefill(q, k, v, cfg.block_size, cfg.topk, workspace=junk,
+                             query_chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(one, part)
+    idx = moba.moba_gate(q, k, cfg.block_size, cfg.topk)
+    rows = oracle.all_rows(cfg.batch, cfg.hq, cfg.seqlen)
+    check_rows(cfg, host_arrays(inp), part.cpu(), idx.cpu(), rows, tag=f"{cfg.name}/c{chunk}")
 
 
 @pytest.mark.parametrize("cfg", [
@@ -207,3 +241,40 @@ def test_full_size_sampled(which, dev):
     torch.cuda.empty_cache()
     rows = sample_rows(cfg, tile=32, n_random=256)
     check_rows(cfg, host_arrays(host), out_h, idx_h, rows)
+
+
+@pytest.mark.timeout(400)
+def test_10m_chunked_sampled(dev):
+    """10M tokens through the query-chunked prefill (256K-token chunks), as the
+    bench times it; sampled rows of three query heads (three KV heads) checked
+    against the oracle run per head (heads are independent in every stage)."""
+    from synth import config_by_name
+    cfg = config_by_name("moba-10m-gqa32x8-d128")
+    chunk = 1 << 18
+    if torch.cuda.get_device_properties(dev).total_memory < 260e9:
+        pytest.skip("needs a 288 GB GPU")
+    moba = _moba()
+    log(f"case {cfg.name}: generating on GPU")
+    inp = make_inputs(cfg, device=dev)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    out = moba.moba_prefill(q, k, v, cfg.block_size, cfg.topk, query_chunk=chunk)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"case {cfg.name}: chunked prefill done")
+    idx = moba.moba_gate(q, k, cfg.block_size, cfg.topk)
+    torch.cuda.synchronize()
+    one = dataclasses.replace(cfg, hq=1, hkv=1)
+    rng = np.random.Generator(np.random.PCG64(cfg.seed + 5))
+    B, n, S = cfg.block_size, cfg.n_blocks, cfg.seqlen
+    for h in (0, 13, 31):
+        g = h // cfg.group
+        host = {"q": q[:, :, h:h + 1].cpu(), "k": k[:, :, g:g + 1].cpu(),
+                "v": v[:, :, g:g + 1].cpu()}
+        out_h, idx_h = out[:, :, h:h + 1].cpu(), idx[:, h:h + 1].cpu()
+        ts = [blk * B + t for blk in (0, cfg.topk - 1, cfg.topk, n // 2, n - 1)
+              for t in range(32)]
+        ts += rng.integers(0, S, 64).tolist()
+        # block boundaries of chunks: the first and last rows of a middle chunk
+        ts += [5 * chunk - 1, 5 * chunk, 5 * chunk + 1, S - 1]
+        rows = np.unique(np.array([(0, 0, t) for t in ts], dtype=np.int64), axis=0)
+        check_rows(one, host_arrays(host), out_h, idx_h, rows, tag=f"{cfg.name}/head{h}")

@@ -55,3 +55,33 @@ def test_sample_rows_cover_strata():
     assert len(np.unique(rows, axis=0)) == len(rows)
     blocks = set((rows[:, 2] // cfg.block_size).tolist())
     assert {0, cfg.topk - 1, cfg.topk, cfg.n_blocks - 1} <= blocks
+
+
+def test_sliced_generation_keeps_the_recipe():
+    """Slices that cut through blocks plant the same blocks with the same statistics."""
+    import dataclasses
+    whole = CONFIGS[0]
+    cfg = dataclasses.replace(whole, gen_slice=320)      # 1024 tokens, block 128: ragged slices
+    a, b = make_inputs(cfg), make_inputs(cfg)
+    for key in ("q", "k", "v"):
+        assert torch.equal(a[key], b[key])
+        assert a[key].shape == make_inputs(whole)[key].shape
+    np.testing.assert_array_equal(a["planted"], make_inputs(whole)["planted"])
+    q, k = a["q"].double(), a["k"].double()
+    B = cfg.block_size
+    for g in range(cfg.hkv):
+        p = int(a["planted"][0, g, 0])
+        kb = k[0, p * B:(p + 1) * B, g].mean(0)
+        assert abs(kb.norm().item() - 2.0) < 0.1
+        u = kb / kb.norm()
+        frac = ((q[0, (p + 1) * B:, g] @ u) > 0.5).double().mean().item()
+        assert 0.15 < frac < 0.35
+        if p > 0:
+            assert ((q[0, :p * B, g] @ u) > 0.5).double().mean().item() < 0.01
+    # unplanted keys stay N(0, 1/d)
+    mask = torch.ones(cfg.seqlen, dtype=torch.bool)
+    for g in range(cfg.hkv):
+        p = int(a["planted"][0, g, 0])
+        mask[p * B:(p + 1) * B] = False
+    rest = k[0, mask].reshape(-1)
+    assert abs(rest.var().item() * cfg.head_dim - 1.0) < 0.05
