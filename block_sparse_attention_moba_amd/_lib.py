@@ -24,7 +24,7 @@ MOBA_NUM_STAGES = 5
 STAGE_NAMES = ("pool", "gate", "index", "attn_past", "attn_own_merge")
 EXPORTS = ("moba_abi_version", "moba_status_string", "moba_workspace_size", "moba_pool",
            "moba_gate", "moba_prefill", "moba_prefill_timed", "moba_workspace_size_chunked",
-           "moba_prefill_chunked")
+           "moba_prefill_chunked", "moba_workspace_size_varlen", "moba_prefill_varlen")
 
 
 class MobaError(RuntimeError):
@@ -65,6 +65,11 @@ def lib():
     L.moba_workspace_size_chunked.argtypes = [ci] * 9 + [ctypes.POINTER(sz)]
     L.moba_prefill_chunked.restype = ci
     L.moba_prefill_chunked.argtypes = [vp, vp, vp, vp] + [ci] * 9 + [vp, sz, vp]
+    ip = ctypes.POINTER(ci)
+    L.moba_workspace_size_varlen.restype = ci
+    L.moba_workspace_size_varlen.argtypes = [ip] + [ci] * 8 + [ctypes.POINTER(sz)]
+    L.moba_prefill_varlen.restype = ci
+    L.moba_prefill_varlen.argtypes = [vp, vp, vp, vp, ip] + [ci] * 8 + [vp, sz, vp]
     _lib = L
     return L
 
@@ -125,6 +130,58 @@ def moba_workspace_size_chunked(batch, seqlen, num_q_heads, num_kv_heads, head_d
                                              ctypes.byref(pb)),
            "moba_workspace_size_chunked")
     return pb.value
+
+
+def _cu_array(cu_seqlens):
+    vals = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist")
+                             else cu_seqlens)]
+    return (ctypes.c_int * len(vals))(*vals), len(vals) - 1
+
+
+def moba_workspace_size_varlen(cu_seqlens, num_q_heads, num_kv_heads, head_dim, block_size,
+                               topk, query_chunk, dtype=MOBA_DTYPE_BF16):
+    """Workspace bytes of moba_prefill_varlen; cu_seqlens: host offsets [num_seqs + 1]."""
+    arr, ns = _cu_array(cu_seqlens)
+    pb = ctypes.c_size_t(0)
+    _check(lib().moba_workspace_size_varlen(arr, ns, num_q_heads, num_kv_heads, head_dim,
+                                            block_size, topk, dtype, query_chunk,
+                                            ctypes.byref(pb)), "moba_workspace_size_varlen")
+    return pb.value
+
+
+def moba_prefill_varlen(q, k, v, cu_seqlens, block_size, topk, out=None, workspace=None,
+                        query_chunk=None):
+    """MoBA prefill of packed sequences: q [total, hq, d], k/v [total, hkv, d] -> out like q.
+
+    cu_seqlens: host sequence offsets (list or CPU tensor) [num_seqs + 1], starting at 0.
+    query_chunk: tokens per query chunk within a sequence (None: whole sequences).
+    """
+    _need_cuda(q, k, v)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or k.shape[0] != q.shape[0]:
+        raise ValueError("q must be [total, hq, d] and k, v [total, hkv, d]")
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    arr, ns = _cu_array(cu_seqlens)
+    if arr[ns] != total:
+        raise ValueError(f"cu_seqlens ends at {arr[ns]}, tensors hold {total} tokens")
+    dt = _dtype_code(q)
+    chunk = max(arr[i + 1] - arr[i] for i in range(ns)) if query_chunk is None else query_chunk
+    if query_chunk is None:
+        chunk = max(block_size, -(-chunk // block_size) * block_size)
+    pb = moba_workspace_size_varlen(cu_seqlens, hq, hkv, d, block_size, topk, chunk, dt)
+    ws = _workspace(pb, q.device, workspace)
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda(out)
+    if out.dtype != q.dtype or out.shape != q.shape:
+        raise ValueError("out must match q in shape and dtype")
+    _check(lib().moba_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), arr, ns, hq, hkv, d,
+                                     block_size, topk, dt, chunk, _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream()),
+           "moba_prefill_varlen")
+    return out
 
 
 def _workspace(nbytes, device, workspace):

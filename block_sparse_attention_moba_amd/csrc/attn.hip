@@ -79,7 +79,7 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, T
     if (tile >= a.ntiles) return false;
     if (mode == kOwn) {
         const int tpb = (a.B + a.M - 1) / a.M;
-        const int nr = a.R / a.B;       // blocks of the chunk
+        const int nr = (a.R + a.B - 1) / a.B;       // blocks of the chunk
         unsigned rest = tile;
         const int tt = rest % tpb; rest /= tpb;
         const int hh = rest % a.G; rest /= a.G;
@@ -88,7 +88,8 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, T
         tl.b = rest / a.Hkv;
         tl.h = tl.g * a.G + hh;
         tl.t0 = i * a.B + tt * a.M;
-        tl.tend = i * a.B + a.B;
+        tl.tend = min(i * a.B + a.B, a.S);     // a short last block ends at S
+        if (tl.t0 >= tl.tend) return false;    // tiles past the end of a short block
         tl.key_begin = i * a.B;
         tl.npast = min(a.topk - 1, i);
     } else {

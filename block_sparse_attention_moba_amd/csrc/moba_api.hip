@@ -24,11 +24,13 @@ struct Layout {
 };
 
 // Past selections over the rows of the chunk: every row in block i keeps
-// min(topk - 1, i) past blocks.
+// min(topk - 1, i) past blocks (the last block may hold fewer than B rows).
 unsigned long long past_rows(const Problem &p) {
     unsigned long long per_seq = 0;
-    for (int i = p.r0 / p.B; i < (p.r0 + p.R) / p.B; ++i) per_seq += (unsigned long long)min(p.topk - 1, i);
-    return per_seq * (unsigned long long)p.B * p.Hq * p.batch;
+    const int end = p.r0 + p.R;
+    for (int i = p.r0 / p.B; i * p.B < end; ++i)
+        per_seq += (unsigned long long)min(p.topk - 1, i) * (unsigned long long)(min(end, (i + 1) * p.B) - i * p.B);
+    return per_seq * p.Hq * p.batch;
 }
 
 size_t elem_size(const Problem &p) { return p.dtype == kBF16 ? 2 : 4; }
@@ -48,12 +50,12 @@ moba_status_t make_problem(int batch, int S, int Hq, int Hkv, int D, int B, int 
     if (Hq % Hkv != 0) return MOBA_ERR_INVALID_ARGUMENT;
     if (dt != MOBA_DTYPE_BF16 && dt != MOBA_DTYPE_FP32) return MOBA_ERR_INVALID_ARGUMENT;
     if (D != 64 && D != 128) return MOBA_ERR_UNSUPPORTED;
-    if (B % 64 != 0 || S % B != 0) return MOBA_ERR_UNSUPPORTED;
+    if (B % 64 != 0 || S % 64 != 0) return MOBA_ERR_UNSUPPORTED;
     if ((long long)S > kMaxSeq) return MOBA_ERR_UNSUPPORTED;
     p->batch = batch; p->S = S; p->Hq = Hq; p->Hkv = Hkv; p->D = D; p->B = B; p->topk = topk;
     p->dtype = (dt == MOBA_DTYPE_BF16) ? kBF16 : kF32;
     p->G = Hq / Hkv;
-    p->n = S / B;
+    p->n = (S + B - 1) / B;
     p->dense = topk >= p->n;
     p->npast = min(topk - 1, p->n - 1);
     p->r0 = 0;
@@ -160,6 +162,28 @@ struct Events {
     }
 };
 
+// Checks every sequence of a variable-length batch (host only) and returns the
+// largest chunked workspace any of them needs.
+moba_status_t varlen_check(const int *cu, int num_seqs, int Hq, int Hkv, int D, int B, int topk,
+                           moba_dtype_t dt, int query_chunk, size_t *ws_bytes) {
+    if (!cu || num_seqs <= 0 || cu[0] != 0) return MOBA_ERR_INVALID_ARGUMENT;
+    if (query_chunk <= 0) return MOBA_ERR_INVALID_ARGUMENT;
+    size_t need = 0;
+    for (int i = 0; i < num_seqs; ++i) {
+        const long long len = (long long)cu[i + 1] - cu[i];
+        if (len < 0) return MOBA_ERR_INVALID_ARGUMENT;
+        if (len == 0) continue;
+        if (len > kMaxSeq || len % 64 != 0) return MOBA_ERR_UNSUPPORTED;
+        Problem p;
+        const moba_status_t rc = make_problem(1, (int)len, Hq, Hkv, D, B, topk, dt, &p);
+        if (rc != MOBA_OK) return rc;
+        if (query_chunk % B != 0) return MOBA_ERR_UNSUPPORTED;
+        need = std::max(need, prefill_layout(p, chunk_len(p, query_chunk)).total);
+    }
+    *ws_bytes = need;
+    return MOBA_OK;
+}
+
 moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *out, int batch,
                            int S, int Hq, int Hkv, int D, int B, int topk, moba_dtype_t dt,
                            int query_chunk, void *ws, size_t ws_bytes, void *stream,
@@ -167,7 +191,8 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
     Problem p;
     moba_status_t rc = make_problem(batch, S, Hq, Hkv, D, B, topk, dt, &p);
     if (rc != MOBA_OK) return rc;
-    if (query_chunk % B != 0) return MOBA_ERR_UNSUPPORTED;
+    // query_chunk 0: one pass over the whole sequence (moba_prefill)
+    if (query_chunk != 0 && query_chunk % B != 0) return MOBA_ERR_UNSUPPORTED;
     const int C = chunk_len(p, query_chunk);
     if (!q || !k || !v || !out) return MOBA_ERR_INVALID_ARGUMENT;
     const size_t qbytes = (size_t)batch * S * Hq * D * elem_size(p);
@@ -315,7 +340,7 @@ moba_status_t moba_gate(const void *q, const void *k, int32_t *block_idx, int ba
 moba_status_t moba_prefill(const void *q, const void *k, const void *v, void *out, int batch,
                            int S, int Hq, int Hkv, int D, int B, int topk, moba_dtype_t dt,
                            void *ws, size_t ws_bytes, void *stream) {
-    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, S, ws, ws_bytes, stream,
+    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, 0, ws, ws_bytes, stream,
                         nullptr);
 }
 
@@ -335,8 +360,55 @@ moba_status_t moba_prefill_timed(const void *q, const void *k, const void *v, vo
     if (!stage_events) return MOBA_ERR_INVALID_ARGUMENT;
     for (int i = 0; i <= MOBA_NUM_STAGES; ++i)
         if (!stage_events[i]) return MOBA_ERR_INVALID_ARGUMENT;
-    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, S, ws, ws_bytes, stream,
+    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, 0, ws, ws_bytes, stream,
                         stage_events);
+}
+
+moba_status_t moba_workspace_size_varlen(const int *cu_seqlens, int num_seqs, int Hq, int Hkv,
+                                         int D, int B, int topk, moba_dtype_t dt,
+                                         int query_chunk, size_t *prefill_bytes) {
+    size_t need = 0;
+    const moba_status_t rc =
+        varlen_check(cu_seqlens, num_seqs, Hq, Hkv, D, B, topk, dt, query_chunk, &need);
+    if (rc != MOBA_OK) return rc;
+    if (!prefill_bytes) return MOBA_ERR_INVALID_ARGUMENT;
+    *prefill_bytes = need;
+    return MOBA_OK;
+}
+
+moba_status_t moba_prefill_varlen(const void *q, const void *k, const void *v, void *out,
+                                  const int *cu_seqlens, int num_seqs, int Hq, int Hkv, int D,
+                                  int B, int topk, moba_dtype_t dt, int query_chunk, void *ws,
+                                  size_t ws_bytes, void *stream) {
+    size_t need = 0;
+    moba_status_t rc =
+        varlen_check(cu_seqlens, num_seqs, Hq, Hkv, D, B, topk, dt, query_chunk, &need);
+    if (rc != MOBA_OK) return rc;
+    if (!q || !k || !v || !out) return MOBA_ERR_INVALID_ARGUMENT;
+    const size_t es = dt == MOBA_DTYPE_BF16 ? 2 : 4;
+    const size_t total = (size_t)cu_seqlens[num_seqs];
+    const size_t qbytes = total * Hq * D * es, kvbytes = total * Hkv * D * es;
+    if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kvbytes) ||
+        overlaps(out, qbytes, v, kvbytes))
+        return MOBA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return MOBA_ERR_UNSUPPORTED;
+    if (ws_bytes < need) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    if (!ws && need > 0) return MOBA_ERR_INVALID_ARGUMENT;
+    if (!aligned(ws, kAlign)) return MOBA_ERR_UNSUPPORTED;
+    // every sequence passed the checks above, so no call below fails them
+    for (int i = 0; i < num_seqs; ++i) {
+        const int len = cu_seqlens[i + 1] - cu_seqlens[i];
+        if (len == 0) continue;
+        const size_t t0 = (size_t)cu_seqlens[i];
+        rc = prefill_impl(static_cast<const char *>(q) + t0 * Hq * D * es,
+                          static_cast<const char *>(k) + t0 * Hkv * D * es,
+                          static_cast<const char *>(v) + t0 * Hkv * D * es,
+                          static_cast<char *>(out) + t0 * Hq * D * es, 1, len, Hq, Hkv, D, B,
+                          topk, dt, query_chunk, ws, ws_bytes, stream, nullptr);
+        if (rc != MOBA_OK) return rc;
+    }
+    return MOBA_OK;
 }
 
 }  // extern "C"

@@ -27,7 +27,7 @@ __host__ __device__ inline uint32_t row_slot(uint64_t r) { return (uint32_t)(r >
 struct Problem {
     int batch, S, Hq, Hkv, D, B, topk, dtype;
     int G;       // Hq / Hkv
-    int n;       // S / B
+    int n;       // ceil(S / B): the last block may be short (S % B tokens)
     int npast;   // topk - 1 capped at n - 1
     bool dense;  // topk >= n: plain causal attention
     // query rows handled by one pass of the sparse stages: tokens [r0, r0 + R),
@@ -82,7 +82,7 @@ inline int tile_rows(const Problem &p) { return p.dtype == kBF16 ? 256 : 128; }
 
 // Tiles of each attention launch (the past-block count is an upper bound).
 inline unsigned long long own_tiles(const Problem &p) {
-    return (unsigned long long)p.batch * p.Hkv * (p.R / p.B) * p.G *
+    return (unsigned long long)p.batch * p.Hkv * ((p.R + p.B - 1) / p.B) * p.G *
            ((p.B + tile_rows(p) - 1) / tile_rows(p));
 }
 inline unsigned long long dense_tiles(const Problem &p) {

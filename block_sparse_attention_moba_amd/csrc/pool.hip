@@ -7,7 +7,7 @@
 // D/8 lanes, so a wave reads 64 x 16 contiguous bytes per step) and writes
 // the chunk's fp32 column sums and the largest squared key norm of the chunk.
 // pool_finalize: sums the chunk partials of a block in a fixed order and
-// divides by the block size, writes the mean also as a bf16 hi + lo pair (the
+// divides by the block's token count (B, or S mod B for a short last block), writes the mean also as a bf16 hi + lo pair (the
 // operands of the matrix-core gate), and takes the block's largest squared key
 // norm (the attention kernels bound every logit of the block by it).  No atomics,
 // so the result is bitwise reproducible.
@@ -54,7 +54,8 @@ __global__ __launch_bounds__(256) void pool_partial_kernel(const T *__restrict__
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     float nmax = 0.f;
     const int t0 = j * B + chunk * CT;
-    for (int t = t0 + tr; t < t0 + CT; t += TPP) {
+    const int t1 = min(t0 + CT, S);              // a short last block ends at S
+    for (int t = t0 + tr; t < t1; t += TPP) {
         float f[8];
         load8(k + (((size_t)b * S + t) * Hkv + g) * D + vec * 8, f);
         float sq = 0.f;
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(256) void pool_finalize_kernel(const float *__restr
                                                             float *__restrict__ kmax2,
                                                             __bf16 *__restrict__ khl,
                                                             long long total, int D, int nchunk,
-                                                            int B) {
+                                                            int B, int S, int n) {
     const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
     if (e >= total) return;
     const long long blk = e / D;
@@ -101,7 +102,8 @@ __global__ __launch_bounds__(256) void pool_finalize_kernel(const float *__restr
     const float *src = partial + (size_t)blk * nchunk * D + i;
     float s = 0.f;
     for (int c = 0; c < nchunk; ++c) s += src[(size_t)c * D];
-    const float m = s / (float)B;
+    const int j = (int)(blk % n);
+    const float m = s / (float)min(B, S - j * B);   // tokens present in block j
     kbar[e] = m;
     // bf16 split for the matrix-core gate: m = hi + lo + O(2^-17 |m|)
     const __bf16 hi = (__bf16)m;
@@ -124,7 +126,7 @@ static hipError_t pool_impl(const void *k, const PoolBuffers &pb, const Problem 
                                                     pb.partial_nmax, p.S, p.Hkv, p.B, p.n, CT);
     const long long total = (long long)p.batch * p.Hkv * p.n * D;
     pool_finalize_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(
-        pb.partial, pb.partial_nmax, pb.kbar, pb.kmax2, pb.khl, total, D, nchunk, p.B);
+        pb.partial, pb.partial_nmax, pb.kbar, pb.kmax2, pb.khl, total, D, nchunk, p.B, p.S, p.n);
     return hipGetLastError();
 }
 

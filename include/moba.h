@@ -15,8 +15,13 @@
  * selected the result is full causal attention (the seamless full / sparse
  * switch the write-up and the overview describe).
  *
+ * Blocks.  Block j holds tokens [j * block_size, (j + 1) * block_size); there
+ * are n = ceil(seqlen / block_size) blocks, and when block_size does not
+ * divide seqlen the last block is short (seqlen mod block_size tokens).  A
+ * short last block is only ever a query's own block, never a past block.
+ *
  * Readings fixed by this library where the pages are silent:
- *   - block key = mean of the block's keys (fp32);
+ *   - block key = mean of the block's keys over the tokens present (fp32);
  *   - gate score = <q, mean key>, unscaled, for past blocks j < t / block_size;
  *   - `topk` counts the own block: a query uses its own block plus the
  *     min(topk - 1, t / block_size) best-scoring past blocks; ties go to the
@@ -30,7 +35,7 @@
  *   block_idx (int32) [batch][num_q_heads][seqlen][topk]: the selected
  *           blocks of each query row, ascending, own block included (it is
  *           the last valid entry), then -1 padding.
- *   kbar (fp32) [batch][num_kv_heads][seqlen / block_size][head_dim].
+ *   kbar (fp32) [batch][num_kv_heads][n][head_dim].
  *
  * Ownership.  Every pointer is caller-owned device memory.  The library
  * allocates nothing, keeps no state between calls and is reentrant: calls on
@@ -44,10 +49,9 @@
  *   MOBA_ERR_INVALID_ARGUMENT   null pointer, a size <= 0, num_q_heads not a
  *                               multiple of num_kv_heads, unknown dtype,
  *                               `out` overlapping an input;
- *   MOBA_ERR_UNSUPPORTED        head_dim not 64 or 128; seqlen not a multiple
- *                               of block_size; block_size not a multiple of
- *                               64; seqlen > 2^24; topk > 32 while topk <
- *                               seqlen / block_size; a pointer not 16-byte
+ *   MOBA_ERR_UNSUPPORTED        head_dim not 64 or 128; seqlen or block_size
+ *                               not a multiple of 64; seqlen > 2^24; topk >
+ *                               32 while topk < n; a pointer not 16-byte
  *                               aligned;
  *   MOBA_ERR_WORKSPACE_TOO_SMALL  workspace_bytes below moba_workspace_size;
  *   MOBA_ERR_HIP                a kernel launch was rejected.
@@ -103,7 +107,8 @@ moba_status_t moba_workspace_size(int batch, int seqlen, int num_q_heads, int nu
 
 /*
  * Block means of the keys: kbar[b][g][j][:] = mean of k[b][t][g][:] over the
- * block_size tokens t of block j, accumulated in fp32 (the "aggregated
+ * tokens t of block j (block_size of them, fewer in a short last block),
+ * accumulated in fp32 (the "aggregated
  * representation of the block keys" of the overview, section "技術細節與優勢").
  * Workspace: at least *gate_bytes of moba_workspace_size.
  */
@@ -127,8 +132,8 @@ moba_status_t moba_gate(const void *q, const void *k, int32_t *block_idx, int ba
 
 /*
  * Whole MoBA causal prefill forward: out = softmax attention of each query
- * over the tokens t' <= t of its selected blocks.  topk >= seqlen /
- * block_size gives exact full causal attention (no gating is run).
+ * over the tokens t' <= t of its selected blocks.  topk >= n gives exact full
+ * causal attention (no gating is run).
  * bf16 inputs: scores and softmax in fp32, P and V products in bf16 on the
  * matrix cores with fp32 accumulation, partial outputs kept in bf16, output
  * rounded to bf16 (nearest even).  fp32 inputs: fp32 throughout.
@@ -143,8 +148,8 @@ moba_status_t moba_prefill(const void *q, const void *k, const void *v, void *ou
  * moba_prefill that also records caller-created hipEvent_t handles on
  * `stream`: stage_events[s] just before stage s (MOBA_STAGE_*) and
  * stage_events[MOBA_NUM_STAGES] after the last stage; stages that a problem
- * does not need record back-to-back events.  With topk >= seqlen /
- * block_size the full causal attention is timed as MOBA_STAGE_ATTN_PAST.  stage_events must hold
+ * does not need record back-to-back events.  With topk >= n the full causal
+ * attention is timed as MOBA_STAGE_ATTN_PAST.  stage_events must hold
  * MOBA_NUM_STAGES + 1 valid events.
  */
 moba_status_t moba_prefill_timed(const void *q, const void *k, const void *v, void *out,
@@ -161,8 +166,7 @@ moba_status_t moba_prefill_timed(const void *q, const void *k, const void *v, vo
  * context, 10M tokens, needs about 1 TB of partial outputs in one pass).  The
  * output is the same as moba_prefill's, bit for bit.  query_chunk: tokens per
  * chunk, a positive multiple of block_size (>= seqlen: one chunk).  Full
- * causal attention (topk >= seqlen / block_size) needs no chunking and
- * ignores it.  Errors as moba_prefill, plus INVALID_ARGUMENT for
+ * causal attention (topk >= n) needs no chunking and ignores it.  Errors as moba_prefill, plus INVALID_ARGUMENT for
  * query_chunk <= 0 and UNSUPPORTED for query_chunk % block_size != 0.
  */
 moba_status_t moba_workspace_size_chunked(int batch, int seqlen, int num_q_heads,
@@ -174,6 +178,33 @@ moba_status_t moba_prefill_chunked(const void *q, const void *k, const void *v, 
                                    int head_dim, int block_size, int topk, moba_dtype_t dtype,
                                    int query_chunk, void *workspace, size_t workspace_bytes,
                                    void *stream);
+
+/*
+ * Variable-length batch: packed sequences of different lengths, each an
+ * independent MoBA prefill with its own blocks (the last one possibly short),
+ * the setting of the write-up's variable-length FlashAttention step.
+ * Sequence i holds tokens [cu_seqlens[i], cu_seqlens[i + 1]) of
+ *   q, out  [total][num_q_heads][head_dim]
+ *   k, v    [total][num_kv_heads][head_dim]     (total = cu_seqlens[num_seqs])
+ * and attends only within itself.  cu_seqlens is a HOST array of num_seqs + 1
+ * offsets, read during the call: cu_seqlens[0] = 0, non-decreasing, every
+ * length a multiple of 64 (empty sequences are skipped).  The sequences run
+ * one after another on `stream`, each over the whole GPU, sharing one
+ * workspace; query_chunk is as in moba_prefill_chunked (per sequence).
+ * Errors as moba_prefill_chunked, checked for every sequence before any HIP
+ * call, plus INVALID_ARGUMENT for a null cu_seqlens, num_seqs <= 0,
+ * cu_seqlens[0] != 0 or a decreasing offset, and UNSUPPORTED for a length
+ * that is not a multiple of 64.
+ */
+moba_status_t moba_workspace_size_varlen(const int *cu_seqlens, int num_seqs, int num_q_heads,
+                                         int num_kv_heads, int head_dim, int block_size,
+                                         int topk, moba_dtype_t dtype, int query_chunk,
+                                         size_t *prefill_bytes);
+moba_status_t moba_prefill_varlen(const void *q, const void *k, const void *v, void *out,
+                                  const int *cu_seqlens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int block_size, int topk,
+                                  moba_dtype_t dtype, int query_chunk, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

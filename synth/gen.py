@@ -142,6 +142,31 @@ def _make_sliced(cfg: Config, dev, seed):
     return {"q": q, "k": k, "v": v, "planted": planted}
 
 
+def make_varlen_inputs(cfg: Config, lengths, device="cpu"):
+    """Packed sequences for the variable-length prefill.
+
+    Sequence i follows ``cfg``'s recipe with seqlen = lengths[i], batch 1 and
+    seed cfg.seed + 7919 * i; the sequences are concatenated along the token
+    axis.  Returns dict(q [T, hq, d], k, v [T, hkv, d], cu_seqlens list [n + 1],
+    configs: the per-sequence Config, None for an empty sequence).
+    """
+    import dataclasses
+    qs, ks, vs, cfgs, cu = [], [], [], [], [0]
+    for i, n in enumerate(lengths):
+        cu.append(cu[-1] + n)
+        if n == 0:
+            cfgs.append(None)
+            continue
+        c = dataclasses.replace(cfg, batch=1, seqlen=n, seed=cfg.seed + 7919 * i)
+        inp = make_inputs(c, device=device)
+        qs.append(inp["q"][0])
+        ks.append(inp["k"][0])
+        vs.append(inp["v"][0])
+        cfgs.append(c)
+    return {"q": torch.cat(qs).contiguous(), "k": torch.cat(ks).contiguous(),
+            "v": torch.cat(vs).contiguous(), "cu_seqlens": cu, "configs": cfgs}
+
+
 def to_oracle_array(t: torch.Tensor):
     """Host numpy view of a bf16 / fp32 tensor as raw storage: (array, code).
 

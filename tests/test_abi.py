@@ -52,7 +52,7 @@ def ws_size(*args):
     ((1, 1024, 2, 2, 64, 128, 0, BF16), INV),        # topk 0
     ((1, 1024, 2, 2, 64, 128, 3, 7), INV),           # dtype
     ((1, 1024, 2, 2, 96, 128, 3, BF16), UNS),        # head_dim
-    ((1, 1000, 2, 2, 64, 128, 3, BF16), UNS),        # S % block
+    ((1, 1000, 2, 2, 64, 128, 3, BF16), UNS),        # S % 64
     ((1, 1024, 2, 2, 64, 32, 3, BF16), UNS),         # block % 64
     ((1, 1 << 25, 2, 2, 64, 4096, 3, BF16), UNS),    # seqlen limit
     ((1, 64 * 64, 2, 2, 64, 64, 40, BF16), UNS),     # topk > 32 while sparse
@@ -60,6 +60,15 @@ def ws_size(*args):
 def test_workspace_size_validation(args, code):
     rc, _, _ = ws_size(*args)
     assert rc == code
+
+
+def test_short_last_block_is_accepted():
+    rc, pb, gb = ws_size(1, 1088, 2, 2, 64, 128, 3, BF16)       # 8 blocks + 64 tokens
+    assert rc == 0 and pb > gb > 0
+    rc2, pb2, _ = ws_size(1, 1024, 2, 2, 64, 128, 3, BF16)
+    assert rc2 == 0 and pb > pb2                                   # a ninth block
+    rc, pb, gb = ws_size(1, 1088, 2, 2, 64, 128, 9, BF16)        # topk >= 9 blocks: dense
+    assert rc == 0 and gb < pb < gb + (1 << 16)
 
 
 def test_workspace_sizes():
@@ -106,6 +115,35 @@ def test_chunked_workspace():
     assert moba.lib().moba_workspace_size_chunked(*dims, 4096, None) == INV
 
 
+def ws_varlen(cu, *rest):
+    arr = (ctypes.c_int * len(cu))(*cu)
+    pb = ctypes.c_size_t(0)
+    rc = moba.lib().moba_workspace_size_varlen(arr, len(cu) - 1, *rest, ctypes.byref(pb))
+    return rc, pb.value
+
+
+def test_varlen_workspace_and_validation():
+    heads = (4, 2, 128, 128, 3, BF16)
+    cu = [0, 640, 1728, 1728, 1792]              # 640, 1088 (short last block), 0, 64
+    rc, pb = ws_varlen(cu, *heads, 1 << 20)
+    assert rc == 0
+    per = [ws_chunked(1, n, *heads, 1 << 20)[1] for n in (640, 1088, 64)]
+    assert pb == max(per)
+    rc, pb2 = ws_varlen(cu, *heads, 256)          # 2-block chunks
+    assert rc == 0 and pb2 <= pb
+    L = moba.lib()
+    assert L.moba_workspace_size_varlen(None, 1, *heads, 256, None) == INV
+    assert ws_varlen([0, 64], *heads, 256)[0] == 0
+    assert ws_varlen([0], *heads, 256)[0] == INV                 # no sequence
+    assert ws_varlen([64, 128], *heads, 256)[0] == INV           # must start at 0
+    assert ws_varlen([0, 128, 64], *heads, 256)[0] == INV        # decreasing
+    assert ws_varlen([0, 100], *heads, 256)[0] == UNS            # length % 64
+    assert ws_varlen([0, 128], *heads, 0)[0] == INV
+    assert ws_varlen([0, 128], *heads, 192)[0] == UNS            # chunk % block
+    arr = (ctypes.c_int * 2)(0, 128)
+    assert L.moba_workspace_size_varlen(arr, 1, *heads, 256, None) == INV
+
+
 FAKE = 1 << 40          # aligned, never dereferenced: every call below fails validation
 
 
@@ -137,6 +175,22 @@ def test_chunked_prefill_rejects_before_any_hip_call():
     assert call(100) == UNS
     assert call(256, nbytes=1024) == WS
     assert call(256, dims=(1, 1024, 2, 2, 80, 128, 3, BF16)) == UNS
+
+
+def test_varlen_prefill_rejects_before_any_hip_call():
+    vp = ctypes.c_void_p
+
+    def call(cu, chunk=256, nbytes=1 << 40, q=FAKE, out=FAKE + (3 << 32), ws=FAKE + (4 << 32)):
+        arr = (ctypes.c_int * len(cu))(*cu)
+        return moba.lib().moba_prefill_varlen(vp(q), vp(FAKE + (1 << 32)), vp(FAKE + (2 << 32)),
+                                              vp(out), arr, len(cu) - 1, 4, 2, 128, 128, 3,
+                                              BF16, chunk, vp(ws), nbytes, None)
+    assert call([0, 640, 1728, 1800]) == UNS    # the last sequence holds 72 tokens
+    assert call([0, 640], q=0) == INV
+    assert call([0, 640], out=FAKE + 64) == INV
+    assert call([0, 640], nbytes=64) == WS
+    assert call([0, 640], chunk=0) == INV
+    assert call([0, 640], ws=FAKE + (4 << 32) + 8) == UNS
 
 
 def test_timed_prefill_needs_events():

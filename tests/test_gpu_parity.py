@@ -102,6 +102,13 @@ EDGE = [
     # more than 256 blocks: the gate keeps running top-k lists instead of block masks
     small("320-blocks-list-gate", hq=4, hkv=1, seqlen=64 * 320, head_dim=128, block_size=64,
           topk=12, planted=12),
+    # a short last block (seqlen not a multiple of block_size)
+    small("short-tail-block", hq=4, hkv=2, seqlen=1088, block_size=128, topk=3),
+    small("short-tail-block192-fp32-d64", hq=2, hkv=1, seqlen=1216, head_dim=64, dtype="fp32",
+          block_size=192, topk=4),
+    small("short-tail-dense", hq=2, hkv=2, seqlen=960, block_size=256, topk=4),
+    small("short-tail-d64-b512", batch=2, hq=2, hkv=2, seqlen=1600, head_dim=64,
+          block_size=512, topk=2),
 ]
 
 
@@ -134,6 +141,7 @@ CHUNKED = [
     (EDGE[4], 256),           # fp32
     (EDGE[5], 7 * 64),        # top-32 over 64 blocks, ragged tail chunk
     (EDGE[7], 96 * 64),       # list gate
+    (EDGE[8], 3 * 128),       # short last block in the tail chunk
 ]
 
 
@@ -156,6 +164,43 @@ def test_chunked_prefill_matches_one_pass(cfg, chunk, dev):
     idx = moba.moba_gate(q, k, cfg.block_size, cfg.topk)
     rows = oracle.all_rows(cfg.batch, cfg.hq, cfg.seqlen)
     check_rows(cfg, host_arrays(inp), part.cpu(), idx.cpu(), rows, tag=f"{cfg.name}/c{chunk}")
+
+
+VARLEN = [
+    # lengths: short last blocks, an empty sequence, a one-block sequence
+    (small("varlen-bf16", hq=4, hkv=2, block_size=128, topk=3), [640, 1088, 0, 64, 1984], None),
+    (small("varlen-bf16-chunked", hq=4, hkv=1, block_size=128, topk=4), [1088, 2048, 192], 256),
+    (small("varlen-fp32-d64", hq=2, hkv=2, head_dim=64, dtype="fp32", block_size=64, topk=3),
+     [448, 64, 1216], None),
+]
+
+
+@pytest.mark.parametrize("cfg,lengths,chunk", VARLEN, ids=lambda c: getattr(c, "name", str(c)))
+def test_varlen_prefill(cfg, lengths, chunk, dev):
+    """Packed sequences: each equals its own moba_prefill bit for bit and the
+    oracle run on that sequence alone, on every row."""
+    from synth import make_varlen_inputs
+    moba = _moba()
+    log(f"case {cfg.name} lengths={lengths} chunk={chunk}")
+    inp = make_varlen_inputs(cfg, lengths)
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    cu = inp["cu_seqlens"]
+    out = moba.moba_prefill_varlen(q, k, v, cu, cfg.block_size, cfg.topk, query_chunk=chunk)
+    torch.cuda.synchronize()
+    out_h = out.cpu()
+    for i, c in enumerate(inp["configs"]):
+        if c is None:
+            continue
+        sl = slice(cu[i], cu[i + 1])
+        qi, ki, vi = (x[sl].unsqueeze(0).contiguous() for x in (q, k, v))
+        alone = moba.moba_prefill(qi, ki, vi, c.block_size, c.topk)
+        idx = moba.moba_gate(qi, ki, c.block_size, c.topk)
+        torch.cuda.synchronize()
+        assert torch.equal(alone[0].cpu(), out_h[sl]), f"sequence {i}"
+        host = {"q": qi.cpu(), "k": ki.cpu(), "v": vi.cpu()}
+        rows = oracle.all_rows(1, c.hq, c.seqlen)
+        check_rows(c, host_arrays(host), out_h[sl].unsqueeze(0), idx.cpu(), rows,
+                   tag=f"{cfg.name}/seq{i}")
 
 
 @pytest.mark.parametrize("cfg", [
