@@ -8,6 +8,11 @@ block 4096, top-k 12).  Prints one JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-dense] [--no-cpu] [--no-secondary] [--query-chunk T]
 
+--workload moba-varlen-1m-gqa32x8-d128 times a packed batch of 7 sequences
+(about 1.09M tokens, every one ending in a short block) through
+moba_prefill_varlen, whole steps timed with HIP events, and the same batch
+with every block selected as its dense comparison.
+
 --workload moba-10m-gqa32x8-d128 times the 10M-token prefill instead: the
 sparse stages run over query chunks of T tokens (default 262144) with one
 chunk's scratch (moba_prefill_chunked), each step timed whole with HIP events;
@@ -39,14 +44,15 @@ def log(msg):
 
 
 def work_counts(cfg):
-    """Algorithmic work of one prefill (selected-block pairs only)."""
+    """Algorithmic work of one prefill (selected-block pairs only; the last
+    block holds S - (n - 1) B rows)."""
     B, n, k, d = cfg.block_size, cfg.n_blocks, cfg.topk, cfg.head_dim
     heads = cfg.hq * cfg.batch
-    past_blocks = sum(min(b, k - 1) for b in range(n)) if k < n else n * (n - 1) // 2
-    past_pairs = B * B * past_blocks * heads
-    own_pairs = n * B * (B + 1) // 2 * heads
-    esz = 2 if cfg.dtype == "bf16" else 4
     S = cfg.seqlen
+    rows = [min(B, S - b * B) for b in range(n)]
+    past_pairs = sum(r * B * min(b, k - 1) for b, r in enumerate(rows)) * heads
+    own_pairs = sum(r * (r + 1) // 2 for r in rows) * heads
+    esz = 2 if cfg.dtype == "bf16" else 4
     return {
         "flops_past": 4.0 * d * past_pairs,
         "flops_own": 4.0 * d * own_pairs,
@@ -196,6 +202,79 @@ def run_chunked(moba, torch, cfg, dev, args):
     print(json.dumps(line), flush=True)
 
 
+def run_varlen(moba, torch, name, dev, args):
+    """A packed variable-length batch: one JSON line from moba_prefill_varlen."""
+    import dataclasses
+    from synth import VARLEN_WORKLOADS, make_varlen_inputs
+    base, lengths = VARLEN_WORKLOADS[name]
+    log(f"{name}: generating {len(lengths)} sequences on the GPU")
+    inp = make_varlen_inputs(base, lengths, device=dev)
+    q, k, v, cu = inp["q"], inp["k"], inp["v"], inp["cu_seqlens"]
+    total = cu[-1]
+    chunk = -(-max(lengths) // base.block_size) * base.block_size
+    ws_bytes = moba.moba_workspace_size_varlen(cu, base.hq, base.hkv, base.head_dim,
+                                               base.block_size, base.topk, chunk)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    call = lambda topk: moba.moba_prefill_varlen(q, k, v, cu, base.block_size, topk, out=out,
+                                                 workspace=ws, query_chunk=chunk)
+    for i in range(args.warmup):
+        call(base.topk)
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        call(base.topk)
+        ev[s][1].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    ms_ev = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    seqs = [c for c in inp["configs"] if c is not None]
+    flops = sum(work_counts(c)["flops_total"] for c in seqs)
+    line = {
+        "metric": METRIC,
+        "value": total / (ms / 1000.0),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": base.dtype,
+        "data": "synthetic (seeded Gaussian Q/K/V with planted high-affinity blocks)",
+        "config": {"workload": name, "total_tokens": total, "seq_lens": lengths,
+                   "num_q_heads": base.hq, "num_kv_heads": base.hkv,
+                   "head_dim": base.head_dim, "block_size": base.block_size,
+                   "topk": base.topk, "parallelism": "single-gpu"},
+        "roofline": {"kernel": "whole varlen prefill (all stages, every sequence)",
+                     "bound": "mfma", "achieved": flops / (ms_ev / 1000.0) / 1e12,
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / (ms_ev / 1000.0) / 1e12 / BF16_PEAK_TFLOPS,
+                     "traffic": None, "avg_launch_ms": round(ms_ev, 3)},
+        "selected_tflop": flops / 1e12,
+    }
+    if not args.no_dense:
+        dense_topk = max(c.n_blocks for c in seqs)
+        call(dense_topk)                              # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        call(dense_topk)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1)
+        log(f"{name}: dense causal {dense_ms:.1f} ms")
+        line["dense_causal_ms"] = round(dense_ms, 3)
+        line["speedup_vs_dense"] = dense_ms / ms
+    print(json.dumps(line), flush=True)
+
+
 def time_dense(moba, torch, cfg, q, k, v):
     """Full causal attention on the same inputs (topk = number of blocks)."""
     out = torch.empty_like(q)
@@ -337,6 +416,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4,
                           "launches": 3}), flush=True)
+        return
+    from synth import VARLEN_WORKLOADS
+    if args.workload in VARLEN_WORKLOADS:
+        run_varlen(moba, torch, args.workload, dev, args)
         return
     cfg = config_by_name(args.workload)
     if cfg.gen_slice > 0:

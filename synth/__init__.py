@@ -5,8 +5,8 @@ of the method's arithmetic (no pooling, gating, selection or attention): both
 the GPU library and the CPU oracle receive the tensors it makes and nothing
 else from it.
 """
-from .configs import CONFIGS, Config, config_by_name
+from .configs import CONFIGS, VARLEN_WORKLOADS, Config, config_by_name
 from .gen import make_inputs, make_varlen_inputs, sample_rows, to_oracle_array
 
-__all__ = ["CONFIGS", "Config", "config_by_name", "make_inputs", "make_varlen_inputs",
+__all__ = ["CONFIGS", "VARLEN_WORKLOADS", "Config", "config_by_name", "make_inputs", "make_varlen_inputs",
            "sample_rows", "to_oracle_array"]

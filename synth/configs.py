@@ -50,6 +50,19 @@ CONFIGS = [
 ]
 
 
+# Packed variable-length batches: (per-sequence recipe, sequence lengths).  The
+# lengths mix long and short prompts, each ending in a short block, for about
+# 1M tokens in all; every sequence uses the 1M workload's heads, block size,
+# top-k and planting (capped by its own block count).
+VARLEN_WORKLOADS = {
+    "moba-varlen-1m-gqa32x8-d128": (
+        Config("moba-varlen-1m-gqa32x8-d128", 1, 32, 8, 0, 128, "bf16", 4096, 12, 16, 0.20,
+               1007),
+        [393216 + 1984, 262144 + 640, 196608 + 3072, 131072 + 64, 65536 + 2048, 32768 + 192,
+         4096 + 960]),
+}
+
+
 def config_by_name(name: str) -> Config:
     for c in CONFIGS:
         if c.name == name:

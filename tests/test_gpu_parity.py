@@ -323,3 +323,26 @@ def test_10m_chunked_sampled(dev):
         ts += [5 * chunk - 1, 5 * chunk, 5 * chunk + 1, S - 1]
         rows = np.unique(np.array([(0, 0, t) for t in ts], dtype=np.int64), axis=0)
         check_rows(one, host_arrays(host), out_h, idx_h, rows, tag=f"{cfg.name}/head{h}")
+
+
+def test_varlen_full_size_sampled(dev):
+    """The packed ~1.09M-token batch the bench times: sampled rows of every
+    sequence against the oracle run on that sequence."""
+    from synth import VARLEN_WORKLOADS, make_varlen_inputs
+    name = "moba-varlen-1m-gqa32x8-d128"
+    base, lengths = VARLEN_WORKLOADS[name]
+    moba = _moba()
+    log(f"case {name}: generating on GPU")
+    inp = make_varlen_inputs(base, lengths, device=dev)
+    q, k, v, cu = inp["q"], inp["k"], inp["v"], inp["cu_seqlens"]
+    out = moba.moba_prefill_varlen(q, k, v, cu, base.block_size, base.topk)
+    torch.cuda.synchronize()
+    log(f"case {name}: GPU done")
+    for i, c in enumerate(inp["configs"]):
+        sl = slice(cu[i], cu[i + 1])
+        qi, ki = (x[sl].unsqueeze(0).contiguous() for x in (q, k))
+        idx = moba.moba_gate(qi, ki, c.block_size, c.topk).cpu()
+        host = {"q": qi.cpu(), "k": ki.cpu(), "v": v[sl].unsqueeze(0).cpu()}
+        rows = sample_rows(c, tile=8, n_random=64)
+        check_rows(c, host_arrays(host), out[sl].unsqueeze(0).cpu(), idx, rows,
+                   tag=f"{name}/seq{i}")
