@@ -16,6 +16,10 @@ Parity status per function (pins live in tests/test_oracle_pins.py):
                   block-diagonal SDPA when topk == 1, closed forms (first
                   token, block size 1), brute force, V -> aV + c, hull bounds.
   attend_merged   pinned: equals ``attend`` (merge algebra) and the above.
+  backward        pinned: central finite differences of ``attend`` under a fixed
+                  selection (dyadic inputs), torch autograd of dense causal SDPA
+                  in fp64 when every block is selected (GQA), sum rules
+                  (sum of dk = 0, sum of dv = sum of dout per KV head).
 """
 import ctypes
 import os
@@ -60,8 +64,11 @@ def _load():
                       _f64p]
     lib.oracle_selection_gap.argtypes = [vp, ci, _f64p, ci, ci, ci, ci, ci, ci, ci, cll, _i64p,
                                          _i32p, _i32p, _f64p]
+    lib.oracle_backward.argtypes = [vp, vp, vp, ci, _f64p, ci, ci, ci, ci, ci, ci, ci, _i32p,
+                                    _f64p, _f64p, _f64p]
     for f in (lib.oracle_pool, lib.oracle_gate, lib.oracle_attend, lib.oracle_attend_merged,
-              lib.oracle_selection_gap, lib.oracle_num_threads, lib.oracle_abi_version):
+              lib.oracle_selection_gap, lib.oracle_backward, lib.oracle_num_threads,
+              lib.oracle_abi_version):
         f.restype = ci
     _lib = lib
     return lib
@@ -161,6 +168,22 @@ def attend(*args):
 def attend_merged(*args):
     """Per-block softmax partials merged by log-sum-exp: (out [R, d], lse [R])."""
     return _attend(_load().oracle_attend_merged, *args)
+
+
+def backward(q, k, v, code, dout, batch, S, hq, hkv, d, block, topk, idx):
+    """Gradients (dq [b, S, hq, d], dk, dv [b, S, hkv, d], float64) of the attention under
+    the selection idx [b, hq, S, topk] for the upstream gradient dout [b, S, hq, d]."""
+    q, qp = _raw(q, code)
+    k, kp = _raw(k, code)
+    v, vp = _raw(v, code)
+    dout = np.ascontiguousarray(dout, dtype=np.float64).reshape(batch, S, hq, d)
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(batch, hq, S, topk)
+    dq = np.zeros((batch, S, hq, d), dtype=np.float64)
+    dk = np.zeros((batch, S, hkv, d), dtype=np.float64)
+    dv = np.zeros((batch, S, hkv, d), dtype=np.float64)
+    _check(_load().oracle_backward(qp, kp, vp, code, dout, batch, S, hq, hkv, d, block, topk,
+                                   idx, dq, dk, dv), "backward")
+    return dq, dk, dv
 
 
 def prefill(q, k, v, code, batch, S, hq, hkv, d, block, topk, rows=None):

@@ -415,3 +415,105 @@ int oracle_selection_gap(const void *q, int code, const double *kbar, int batch,
     }
     return err;
 }
+
+/*
+ * Gradients of the attention under a supplied selection, for every row.
+ * The write-up trains with MoBA (its continual pre-training and fine-tuning
+ * runs), so the attention has a backward; the selection itself gets none:
+ * the top-k is piecewise constant and the gate has no parameters of its own.
+ * With p_ts the softmax weights over T(t) (as in oracle_attend) and dout the
+ * upstream gradient of out:
+ *   dv_s   = sum over rows (t, h) with s in T(t) of p_ts dout_t
+ *   dp_ts  = dout_t . v_s,   delta_t = sum_s p_ts dp_ts
+ *   ds_ts  = p_ts (dp_ts - delta_t)
+ *   dq_t   = sum_s ds_ts k_s / sqrt(d),   dk_s = sum over rows of ds_ts q_t / sqrt(d)
+ * idx: [batch][hq][S][topk], the layout of the GPU's block_idx.
+ * dout, dq: [batch][S][hq][d]; dk, dv: [batch][S][hkv][d]; all double.
+ * Parallel over (batch, KV head): each owns its dk / dv rows, so no races.
+ */
+int oracle_backward(const void *q, const void *k, const void *v, int code, const double *dout,
+                    int batch, int S, int hq, int hkv, int d, int block, int topk,
+                    const int *idx, double *dq, double *dk, double *dv) {
+    if (!q || !k || !v || !dout || !idx || !dq || !dk || !dv) return 1;
+    if (check_dims(batch, S, hq, hkv, d, block, topk)) return 1;
+    const int n = n_blocks(S, block);
+    const int group = hq / hkv;
+    const double scale = 1.0 / sqrt((double)d);
+    memset(dq, 0, sizeof(double) * (size_t)batch * S * hq * d);
+    memset(dk, 0, sizeof(double) * (size_t)batch * S * hkv * d);
+    memset(dv, 0, sizeof(double) * (size_t)batch * S * hkv * d);
+    int err = 0;
+#pragma omp parallel
+    {
+        char *flag = (char *)malloc((size_t)n);
+        double *p = (double *)malloc(sizeof(double) * (size_t)S);
+        double *dp = (double *)malloc(sizeof(double) * (size_t)S);
+        double *qv = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!flag || !p || !dp || !qv) {
+#pragma omp atomic write
+            err = 3;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (long long bg = 0; bg < (long long)batch * hkv; ++bg) {
+            if (!flag || !p || !dp || !qv) continue;
+            const int b = (int)(bg / hkv), g = (int)(bg % hkv);
+            for (int h = g * group; h < (g + 1) * group; ++h) {
+                for (int t = 0; t < S; ++t) {
+                    const int own = t / block;
+                    const int *sel = idx + (((size_t)b * hq + h) * S + t) * topk;
+                    if (mark_selection(sel, topk, own, flag, n)) {
+#pragma omp atomic write
+                        err = 2;
+                        continue;
+                    }
+                    const size_t qbase = (((size_t)b * S + t) * hq + h) * d;
+                    for (int i = 0; i < d; ++i) qv[i] = load_elem(q, code, qbase + i);
+                    const double *go = dout + qbase;
+                    /* softmax weights over T(t) */
+                    double m = -INFINITY;
+                    for (int s = 0; s <= t; ++s) {
+                        if (!flag[s / block]) continue;
+                        const size_t kb = (((size_t)b * S + s) * hkv + g) * d;
+                        double acc = 0.0;
+                        for (int i = 0; i < d; ++i) acc += qv[i] * load_elem(k, code, kb + i);
+                        p[s] = acc * scale;
+                        if (p[s] > m) m = p[s];
+                    }
+                    double l = 0.0;
+                    for (int s = 0; s <= t; ++s)
+                        if (flag[s / block]) {
+                            p[s] = exp(p[s] - m);
+                            l += p[s];
+                        }
+                    /* dp and delta */
+                    double delta = 0.0;
+                    for (int s = 0; s <= t; ++s) {
+                        if (!flag[s / block]) continue;
+                        p[s] /= l;
+                        const size_t vb = (((size_t)b * S + s) * hkv + g) * d;
+                        double acc = 0.0;
+                        for (int i = 0; i < d; ++i) acc += go[i] * load_elem(v, code, vb + i);
+                        dp[s] = acc;
+                        delta += p[s] * acc;
+                    }
+                    double *gq = dq + qbase;
+                    for (int s = 0; s <= t; ++s) {
+                        if (!flag[s / block]) continue;
+                        const size_t kb = (((size_t)b * S + s) * hkv + g) * d;
+                        const double ds = p[s] * (dp[s] - delta);
+                        for (int i = 0; i < d; ++i) {
+                            gq[i] += ds * load_elem(k, code, kb + i) * scale;
+                            dk[kb + i] += ds * qv[i] * scale;
+                            dv[kb + i] += p[s] * go[i];
+                        }
+                    }
+                }
+            }
+        }
+        free(flag);
+        free(p);
+        free(dp);
+        free(qv);
+    }
+    return err;
+}

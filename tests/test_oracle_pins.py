@@ -357,3 +357,91 @@ def test_comparison_harness_catches_a_swapped_block():
     rep = output_report(out_m[sel_rows], out[sel_rows])
     assert not output_ok(rep, "bf16"), rep
     assert output_ok(output_report(out[sel_rows], out[sel_rows]), "fp32")
+
+
+# ---------------------------------------------------------------- backward
+
+def _selection(q, k, block, topk):
+    """idx [b, hq, S, topk] from the oracle's own gate on every row."""
+    batch, S, hq, d = q.shape
+    rows, idx, _, _, _ = run_oracle(q, k, k, block, topk)
+    return idx.reshape(batch, hq, S, topk)
+
+
+def _loss(q, k, v, dout, block, topk, idx):
+    """sum(dout * out) of the attention under the fixed selection idx."""
+    batch, S, hq, d = q.shape
+    rows = oracle.all_rows(batch, hq, S)
+    out, _ = oracle.attend(q, k, v, 1, batch, S, hq, k.shape[2], d, block, topk, rows,
+                           idx.reshape(-1, topk))
+    out = to_bhtd(out, rows, batch, hq, S, d).transpose(0, 2, 1, 3)
+    return float((dout * out).sum())
+
+
+@pytest.mark.parametrize("S,hq,hkv,d,block,topk", [(16, 2, 1, 4, 4, 2), (24, 2, 2, 4, 8, 2),
+                                                   (20, 4, 2, 2, 4, 3)])
+def test_backward_matches_central_differences(S, hq, hkv, d, block, topk):
+    """Pin: every gradient entry against (L(x + e) - L(x - e)) / 2e of the forward
+    oracle with the selection held fixed.  Inputs are multiples of 2^-6 and
+    e = 2^-14, so x +- e is exact in fp32 storage; the O(e^2) truncation is far
+    below the 1e-6 tolerance."""
+    rng = np.random.default_rng(S * 7 + d)
+    q = (rng.integers(-48, 49, (1, S, hq, d)) / 64.0).astype(np.float32)
+    k = (rng.integers(-48, 49, (1, S, hkv, d)) / 64.0).astype(np.float32)
+    v = (rng.integers(-48, 49, (1, S, hkv, d)) / 64.0).astype(np.float32)
+    dout = rng.standard_normal((1, S, hq, d))
+    idx = _selection(q, k, block, topk)
+    dq, dk, dv = oracle.backward(q, k, v, 1, dout, 1, S, hq, hkv, d, block, topk, idx)
+    e = 2.0 ** -14
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(grad)
+        for pos in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += e
+            xm[pos] -= e
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], dout, block, topk, idx)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], dout, block, topk, idx)
+            fd[pos] = (lp - lm) / (2 * e)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-7, err_msg=f"d{name}")
+
+
+def test_backward_full_selection_equals_sdpa_autograd():
+    """Pin: with every causal block selected the gradients are those of dense
+    causal attention: torch autograd through scaled_dot_product_attention in
+    fp64 (GQA: each query head uses its KV head; the KV gradients add up)."""
+    S, hq, hkv, d, block = 48, 4, 2, 8, 8
+    q, k, v = rand_inputs(S, hq, hkv, d, batch=2, seed=11)
+    dout = np.random.default_rng(3).standard_normal((2, S, hq, d))
+    topk = -(-S // block)
+    idx = _selection(q, k, block, topk)
+    dq, dk, dv = oracle.backward(q, k, v, 1, dout, 2, S, hq, hkv, d, block, topk, idx)
+    G = hq // hkv
+    tq = torch.tensor(q, dtype=torch.float64).transpose(1, 2).requires_grad_()
+    tk = torch.tensor(k, dtype=torch.float64).transpose(1, 2).requires_grad_()
+    tv = torch.tensor(v, dtype=torch.float64).transpose(1, 2).requires_grad_()
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1), is_causal=True)
+    out.backward(torch.tensor(dout, dtype=torch.float64).transpose(1, 2))
+    np.testing.assert_allclose(dq, tq.grad.transpose(1, 2).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.transpose(1, 2).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.transpose(1, 2).numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_sum_rules():
+    """Pin: softmax weights of a row sum to 1, so over all keys of a KV head
+    sum(dv) = sum of dout over its query heads, and sum(dk) = 0 (each row's
+    ds sums to zero)."""
+    S, hq, hkv, d, block, topk = 96, 4, 2, 8, 16, 3
+    q, k, v = rand_inputs(S, hq, hkv, d, seed=5, planted=1, block=block)
+    dout = np.random.default_rng(9).standard_normal((1, S, hq, d))
+    idx = _selection(q, k, block, topk)
+    dq, dk, dv = oracle.backward(q, k, v, 1, dout, 1, S, hq, hkv, d, block, topk, idx)
+    G = hq // hkv
+    for g in range(hkv):
+        np.testing.assert_allclose(dv[0, :, g].sum(0), dout[0, :, g * G:(g + 1) * G].sum((0, 1)),
+                                   rtol=1e-10, atol=1e-10)
+        np.testing.assert_allclose(dk[0, :, g].sum(0), 0.0, atol=1e-10)
+    assert np.abs(dq).max() > 1e-3 and np.abs(dk).max() > 1e-3
