@@ -24,7 +24,8 @@ MOBA_NUM_STAGES = 5
 STAGE_NAMES = ("pool", "gate", "index", "attn_past", "attn_own_merge")
 EXPORTS = ("moba_abi_version", "moba_status_string", "moba_workspace_size", "moba_pool",
            "moba_gate", "moba_prefill", "moba_prefill_timed", "moba_workspace_size_chunked",
-           "moba_prefill_chunked", "moba_workspace_size_varlen", "moba_prefill_varlen")
+           "moba_prefill_chunked", "moba_workspace_size_varlen", "moba_prefill_varlen",
+           "moba_prefill_lse", "moba_workspace_size_backward", "moba_backward")
 
 
 class MobaError(RuntimeError):
@@ -70,6 +71,12 @@ def lib():
     L.moba_workspace_size_varlen.argtypes = [ip] + [ci] * 8 + [ctypes.POINTER(sz)]
     L.moba_prefill_varlen.restype = ci
     L.moba_prefill_varlen.argtypes = [vp, vp, vp, vp, ip] + [ci] * 8 + [vp, sz, vp]
+    L.moba_prefill_lse.restype = ci
+    L.moba_prefill_lse.argtypes = [vp] * 5 + [ci] * 8 + [vp, sz, vp]
+    L.moba_workspace_size_backward.restype = ci
+    L.moba_workspace_size_backward.argtypes = [ci] * 8 + [ctypes.POINTER(sz)]
+    L.moba_backward.restype = ci
+    L.moba_backward.argtypes = [vp] * 9 + [ci] * 8 + [vp, sz, vp]
     _lib = L
     return L
 
@@ -182,6 +189,59 @@ def moba_prefill_varlen(q, k, v, cu_seqlens, block_size, topk, out=None, workspa
                                      ws.numel() * ws.element_size(), _stream()),
            "moba_prefill_varlen")
     return out
+
+
+def moba_prefill_lse(q, k, v, block_size, topk, out=None, lse=None, workspace=None):
+    """moba_prefill that also returns the rows' natural-log log-sum-exp [b, hq, S] (fp32)."""
+    _need_cuda(q, k, v)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    b, S, hq, d = q.shape
+    hkv = k.shape[2]
+    if k.shape != (b, S, hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [batch, seqlen, num_kv_heads, head_dim]")
+    dt = _dtype_code(q)
+    pb, _ = moba_workspace_size(b, S, hq, hkv, d, block_size, topk, dt)
+    ws = _workspace(pb, q.device, workspace)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((b, hq, S), dtype=torch.float32, device=q.device) if lse is None else lse
+    _need_cuda(out, lse)
+    if out.dtype != q.dtype or out.shape != q.shape or lse.shape != (b, hq, S):
+        raise ValueError("out must match q; lse must be float32 [batch, hq, seqlen]")
+    _check(lib().moba_prefill_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, S, hq, hkv,
+                                  d, block_size, topk, dt, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream()), "moba_prefill_lse")
+    return out, lse
+
+
+def moba_workspace_size_backward(batch, seqlen, num_q_heads, num_kv_heads, head_dim, block_size,
+                                 topk, dtype=MOBA_DTYPE_BF16):
+    nb = ctypes.c_size_t(0)
+    _check(lib().moba_workspace_size_backward(batch, seqlen, num_q_heads, num_kv_heads, head_dim,
+                                              block_size, topk, dtype, ctypes.byref(nb)),
+           "moba_workspace_size_backward")
+    return nb.value
+
+
+def moba_backward(q, k, v, out, dout, lse, block_size, topk, workspace=None):
+    """Gradients (dq, dk, dv) of the MoBA attention for the upstream gradient dout (bf16)."""
+    _need_cuda(q, k, v, out, dout, lse)
+    b, S, hq, d = q.shape
+    hkv = k.shape[2]
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise TypeError("q, k, v, out and dout must share a dtype")
+    if out.shape != q.shape or dout.shape != q.shape or k.shape != (b, S, hkv, d) \
+            or v.shape != k.shape or lse.shape != (b, hq, S) or lse.dtype != torch.float32:
+        raise ValueError("shapes: q, out, dout [b, S, hq, d]; k, v [b, S, hkv, d]; lse [b, hq, S]")
+    dt = _dtype_code(q)
+    nb = moba_workspace_size_backward(b, S, hq, hkv, d, block_size, topk, dt)
+    ws = _workspace(nb, q.device, workspace)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check(lib().moba_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
+                               _ptr(dq), _ptr(dk), _ptr(dv), b, S, hq, hkv, d, block_size, topk,
+                               dt, _ptr(ws), ws.numel() * ws.element_size(), _stream()),
+           "moba_backward")
+    return dq, dk, dv
 
 
 def _workspace(nbytes, device, workspace):

@@ -47,6 +47,7 @@ struct AttnArgs {
     float scale_log2;      // log2(e) / sqrt(D)
     unsigned *defer_count;  // tiles whose logit bound fails, for the tracking pass
     unsigned *defer_list;
+    float *lse_out;         // optional natural-log LSE of rows written to the output
 };
 
 struct Tile {
@@ -606,6 +607,8 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
                 if (half == 0) a.part_lse[id] = lse[g];
             } else {
                 dst[g] = (((long long)tl.b * a.S + t[g]) * a.Hq + h[g]) * D;
+                if (a.lse_out && half == 0)
+                    a.lse_out[((long long)tl.b * a.Hq + h[g]) * a.S + t[g]] = lse[g] * kLn2;
             }
         }
     }
@@ -756,6 +759,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     float *dst = static_cast<float *>(a.out) + (((size_t)tl.b * a.S + t) * a.Hq + h) * D + dh * DH;
 #pragma unroll
     for (int i = 0; i < DH; ++i) dst[i] = o[i] * inv;
+    if (a.lse_out && dh == 0) a.lse_out[((long long)tl.b * a.Hq + h) * a.S + t] = lse * kLn2;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -769,6 +773,7 @@ static AttnArgs make_args(const AttnBuffers &bf, const Problem &p) {
     a.kmax2 = bf.kmax2;
     a.defer_count = bf.defer_count;
     a.defer_list = bf.defer_list;
+    a.lse_out = bf.lse_out;
     a.batch = p.batch; a.S = p.S; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.B = p.B; a.n = p.n;
     a.r0 = p.r0; a.R = p.R;
     a.topk = p.topk;

@@ -4,7 +4,8 @@
 // with the softmax renormalisation).  Each partial o_j is normalised within
 // its block and carries its base-2 log-sum-exp l_j; the row's output is
 //     sum_j 2^(l_j - L) o_j,  L = log2 sum_j 2^l_j,
-// taken against the largest l_j for range.  Slots 0 .. npast-1 hold the past
+// taken against the largest l_j for range.  The row's own log-sum-exp L (as a
+// natural log) is also written when the caller asks for it.  Slots 0 .. npast-1 hold the past
 // blocks, slot topk-1 the own block; rows without past blocks were written
 // by the own-block pass directly and are skipped here.
 //
@@ -51,9 +52,10 @@ __device__ inline void store8(float *p, const float *f) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(const T *__restrict__ part_o,
                                                     const float *__restrict__ part_lse,
-                                                    T *__restrict__ out, int S, int Hq, int B,
-                                                    int topk, int nslot, long long rows, int r0,
-                                                    int R) {
+                                                    T *__restrict__ out,
+                                                    float *__restrict__ lse_out, int S, int Hq,
+                                                    int B, int topk, int nslot, long long rows,
+                                                    int r0, int R) {
     constexpr int LPR = D / 8;
     constexpr int RPW = 256 / LPR;
     const long long row = (long long)blockIdx.x * RPW + threadIdx.x / LPR;
@@ -84,6 +86,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const T *__restrict__ part_o
         for (int e = 0; e < 8; ++e) o[e] = fmaf(w, f[e], o[e]);
     }
     const float iw = 1.f / wsum;
+    if (lse_out && ch == 0) lse_out[((size_t)b * Hq + h) * S + t] = (mx + log2f(wsum)) * kLn2;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] *= iw;
     store8(out + (((size_t)b * S + t) * Hq + h) * D + ch * 8, o);
@@ -94,7 +97,8 @@ hipError_t merge_impl(const AttnBuffers &bf, const Problem &p, hipStream_t st) {
     constexpr int RPW = 256 / (D / 8);
     const long long rows = (long long)p.batch * p.Hq * p.R;
     merge_kernel<T, D><<<(unsigned)((rows + RPW - 1) / RPW), 256, 0, st>>>(
-        static_cast<const T *>(bf.part_o), bf.part_lse, static_cast<T *>(bf.out), p.S, p.Hq, p.B,
+        static_cast<const T *>(bf.part_o), bf.part_lse, static_cast<T *>(bf.out), bf.lse_out, p.S,
+        p.Hq, p.B,
         p.topk, part_slots(p), rows, p.r0, p.R);
     return hipGetLastError();
 }

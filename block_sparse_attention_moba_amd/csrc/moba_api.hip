@@ -20,7 +20,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 struct Layout {
     size_t kbar = 0, kmax2 = 0, khl = 0, poolp = 0, pooln = 0, defer = 0, idx = 0, cnt = 0, cursor = 0,
            list_off = 0, tile_off = 0, tile_list = 0, lists = 0, part_o = 0, part_lse = 0,
-           total = 0;
+           l2 = 0, delta = 0, part_dq = 0, total = 0;
 };
 
 // Past selections over the rows of the chunk: every row in block i keeps
@@ -133,6 +133,43 @@ Layout prefill_layout(const Problem &full, int C) {
     return l;
 }
 
+// Workspace of the backward pass: the forward's selection rebuilt (block
+// means, block indices, lists), the per-row base-2 log-sum-exp and dO . O, and
+// the dq partial slots.
+Layout backward_layout(const Problem &p) {
+    Layout l = gate_layout(p);
+    size_t off = l.total;
+    const size_t rows = (size_t)p.batch * p.Hq * p.S;
+    const size_t L = (size_t)p.batch * p.Hkv * p.n;
+    const unsigned long long prow = past_rows(p);
+    l.idx = off; off += align_up(rows * p.topk * 4);
+    l.cnt = off; off += align_up(L * 4);
+    l.cursor = off; off += align_up(L * 4);
+    l.list_off = off; off += align_up((L + 1) * 8);
+    l.tile_off = off; off += align_up((L + 1) * 4);
+    l.tile_list = off; off += align_up((size_t)past_tiles_upper(p, prow) * 4);
+    l.lists = off; off += align_up((size_t)prow * 8);
+    l.l2 = off; off += align_up(rows * 4);
+    l.delta = off; off += align_up(rows * 4);
+    l.part_dq = off; off += align_up(rows * bwd_slots(p) * p.D * 2);
+    l.total = off;
+    return l;
+}
+
+// The backward's problem: bf16 only; a full selection (topk >= n) is run as
+// topk = n through the same lists, so it needs n - 1 <= kMaxPast.
+moba_status_t backward_problem(int batch, int S, int Hq, int Hkv, int D, int B, int topk,
+                               moba_dtype_t dt, Problem *p) {
+    moba_status_t rc = make_problem(batch, S, Hq, Hkv, D, B, topk, dt, p);
+    if (rc != MOBA_OK) return rc;
+    if (dt != MOBA_DTYPE_BF16) return MOBA_ERR_UNSUPPORTED;
+    if (p->dense) {
+        if (p->n - 1 > kMaxPast) return MOBA_ERR_UNSUPPORTED;
+        rc = make_problem(batch, S, Hq, Hkv, D, B, p->n, dt, p);
+    }
+    return rc;
+}
+
 bool aligned(const void *ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -187,7 +224,7 @@ moba_status_t varlen_check(const int *cu, int num_seqs, int Hq, int Hkv, int D, 
 moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *out, int batch,
                            int S, int Hq, int Hkv, int D, int B, int topk, moba_dtype_t dt,
                            int query_chunk, void *ws, size_t ws_bytes, void *stream,
-                           void *const *events) {
+                           void *const *events, float *lse_out = nullptr) {
     Problem p;
     moba_status_t rc = make_problem(batch, S, Hq, Hkv, D, B, topk, dt, &p);
     if (rc != MOBA_OK) return rc;
@@ -200,8 +237,12 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
     if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kvbytes) ||
         overlaps(out, qbytes, v, kvbytes))
         return MOBA_ERR_INVALID_ARGUMENT;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(lse_out, 4))
         return MOBA_ERR_UNSUPPORTED;
+    if (lse_out && (overlaps(lse_out, (size_t)batch * Hq * S * 4, out, qbytes) ||
+                    overlaps(lse_out, (size_t)batch * Hq * S * 4, q, qbytes)))
+        return MOBA_ERR_INVALID_ARGUMENT;
     const Layout l = prefill_layout(p, C);
     if (ws_bytes < l.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
     if (!ws) return MOBA_ERR_INVALID_ARGUMENT;
@@ -217,6 +258,7 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
     bf.kmax2 = pb.kmax2;
     bf.defer_count = reinterpret_cast<unsigned *>(w + l.defer);
     bf.defer_list = reinterpret_cast<unsigned *>(w + l.defer + 256);
+    bf.lse_out = lse_out;
     hipError_t e = hipSuccess;
     if (p.dense) {
         // key-norm bounds (the pool pass), then full causal attention
@@ -409,6 +451,83 @@ moba_status_t moba_prefill_varlen(const void *q, const void *k, const void *v, v
         if (rc != MOBA_OK) return rc;
     }
     return MOBA_OK;
+}
+
+moba_status_t moba_prefill_lse(const void *q, const void *k, const void *v, void *out,
+                               float *lse, int batch, int S, int Hq, int Hkv, int D, int B,
+                               int topk, moba_dtype_t dt, void *ws, size_t ws_bytes,
+                               void *stream) {
+    if (!lse) return MOBA_ERR_INVALID_ARGUMENT;
+    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, 0, ws, ws_bytes, stream,
+                        nullptr, lse);
+}
+
+moba_status_t moba_workspace_size_backward(int batch, int S, int Hq, int Hkv, int D, int B,
+                                           int topk, moba_dtype_t dt, size_t *bytes) {
+    Problem p;
+    const moba_status_t rc = backward_problem(batch, S, Hq, Hkv, D, B, topk, dt, &p);
+    if (rc != MOBA_OK) return rc;
+    if (!bytes) return MOBA_ERR_INVALID_ARGUMENT;
+    *bytes = backward_layout(p).total;
+    return MOBA_OK;
+}
+
+moba_status_t moba_backward(const void *q, const void *k, const void *v, const void *out,
+                            const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                            int batch, int S, int Hq, int Hkv, int D, int B, int topk,
+                            moba_dtype_t dt, void *ws, size_t ws_bytes, void *stream) {
+    Problem p;
+    const moba_status_t rc = backward_problem(batch, S, Hq, Hkv, D, B, topk, dt, &p);
+    if (rc != MOBA_OK) return rc;
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+        return MOBA_ERR_INVALID_ARGUMENT;
+    const size_t qb = (size_t)batch * S * Hq * D * 2, kb = (size_t)batch * S * Hkv * D * 2;
+    const size_t lb = (size_t)batch * Hq * S * 4;
+    const void *in[6] = {q, k, v, out, dout, lse};
+    const size_t inb[6] = {qb, kb, kb, qb, qb, lb};
+    void *outp[3] = {dq, dk, dv};
+    const size_t outb[3] = {qb, kb, kb};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(outp[o], outb[o], in[i], inb[i])) return MOBA_ERR_INVALID_ARGUMENT;
+        for (int o2 = 0; o2 < o; ++o2)
+            if (overlaps(outp[o], outb[o], outp[o2], outb[o2])) return MOBA_ERR_INVALID_ARGUMENT;
+    }
+    for (int i = 0; i < 5; ++i)
+        if (!aligned(in[i], 16)) return MOBA_ERR_UNSUPPORTED;
+    if (!aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+        return MOBA_ERR_UNSUPPORTED;
+    const Layout l = backward_layout(p);
+    if (ws_bytes < l.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    if (!ws) return MOBA_ERR_INVALID_ARGUMENT;
+    if (!aligned(ws, kAlign)) return MOBA_ERR_UNSUPPORTED;
+
+    hipStream_t st = as_stream(stream);
+    char *w = static_cast<char *>(ws);
+    const PoolBuffers pb = pool_buffers(w, l, nullptr);
+    int32_t *idx = reinterpret_cast<int32_t *>(w + l.idx);
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(w + l.cnt);
+    uint32_t *cursor = reinterpret_cast<uint32_t *>(w + l.cursor);
+    uint64_t *list_off = reinterpret_cast<uint64_t *>(w + l.list_off);
+    uint32_t *tile_off = reinterpret_cast<uint32_t *>(w + l.tile_off);
+    uint32_t *tile_list = reinterpret_cast<uint32_t *>(w + l.tile_list);
+    uint64_t *lists = reinterpret_cast<uint64_t *>(w + l.lists);
+    const unsigned long long prow = past_rows(p);
+    const unsigned long long tiles_upper = past_tiles_upper(p, prow);
+    hipError_t e = launch_pool(k, pb, p, st);
+    if (e == hipSuccess) e = launch_gate(q, pb.kbar, pb.khl, idx, p, st);
+    if (e == hipSuccess)
+        e = launch_index(idx, cnt, cursor, list_off, tile_off, tile_list, tiles_upper, lists, p,
+                         st);
+    if (e != hipSuccess) return MOBA_ERR_HIP;
+    BwdBuffers bb;
+    bb.q = q; bb.k = k; bb.v = v; bb.out = out; bb.dout = dout; bb.lse = lse;
+    bb.dq = dq; bb.dk = dk; bb.dv = dv;
+    bb.l2 = reinterpret_cast<float *>(w + l.l2);
+    bb.delta = reinterpret_cast<float *>(w + l.delta);
+    bb.part_dq = w + l.part_dq;
+    bb.lists = lists; bb.list_off = list_off; bb.tile_off = tile_off; bb.tile_list = tile_list;
+    return hip_status(launch_backward(bb, p, prow > 0 ? tiles_upper : 0, st));
 }
 
 }  // extern "C"

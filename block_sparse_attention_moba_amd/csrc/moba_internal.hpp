@@ -13,6 +13,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kMaxPast = 31;
 // Block-count limit for the LDS histograms of the index build.
 constexpr int kHistMax = 4096;
+// ln 2: base-2 log-sum-exps (the kernels' units) to natural logs.
+constexpr float kLn2 = 0.693147180559945309f;
 
 enum DType { kBF16 = 0, kF32 = 1 };
 
@@ -69,6 +71,7 @@ struct AttnBuffers {
     const float *kmax2;     // [batch][Hkv][n] largest squared key norm per block
     unsigned *defer_count;  // deferred-tile list (tiles that need running-max tracking)
     unsigned *defer_list;
+    float *lse_out;         // optional [batch][Hq][S]: natural-log log-sum-exp of each row
 };
 hipError_t launch_attn_past(const AttnBuffers &b, const Problem &p, uint64_t tiles_upper,
                             hipStream_t st);
@@ -76,8 +79,24 @@ hipError_t launch_attn_own(const AttnBuffers &b, const Problem &p, hipStream_t s
 hipError_t launch_attn_dense(const AttnBuffers &b, const Problem &p, hipStream_t st);
 hipError_t launch_merge(const AttnBuffers &b, const Problem &p, hipStream_t st);
 
-// Query rows per attention tile: 4 waves x 64 rows on the bf16 matrix-core
-// path, 256 threads x half a row on the fp32 path.
+// Backward pass (bf16): the forward's selection is rebuilt (pool, gate, index),
+// then dq through partial slots per (row, block) and dk / dv per key.
+struct BwdBuffers {
+    const void *q, *k, *v, *out, *dout;
+    const float *lse;       // [batch][Hq][S] natural-log log-sum-exp from the forward
+    void *dq, *dk, *dv;
+    float *l2, *delta;      // [batch][Hq][S] scratch: lse in base 2, dO . O
+    void *part_dq;          // [batch][Hq][S][slots][D] bf16 scratch
+    const uint64_t *lists;
+    const uint64_t *list_off;
+    const uint32_t *tile_off;
+    const uint32_t *tile_list;
+};
+hipError_t launch_backward(const BwdBuffers &bb, const Problem &p, uint64_t tiles_upper,
+                           hipStream_t st);
+
+// Query rows per attention tile: 256 on the bf16 matrix-core path (8 waves x 32
+// rows for d = 128, 4 x 64 for d = 64), 128 on the fp32 path (two threads a row).
 inline int tile_rows(const Problem &p) { return p.dtype == kBF16 ? 256 : 128; }
 
 // Tiles of each attention launch (the past-block count is an upper bound).
@@ -93,6 +112,8 @@ inline unsigned long long dense_tiles(const Problem &p) {
 // one for the own block (slot topk - 1), which is written only when the row
 // has past blocks to merge with.
 inline int part_slots(const Problem &p) { return p.topk; }
+// Backward dq slots per row: past blocks, then the own block (slot - 1).
+inline int bwd_slots(const Problem &p) { return p.topk < p.n ? p.topk : p.n; }
 
 // Pool partial-sum chunk length (tokens) for a block size that is a multiple of 64.
 inline int pool_chunk(int B) { return (B % 256 == 0) ? 256 : (B % 128 == 0 ? 128 : 64); }

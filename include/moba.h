@@ -206,6 +206,45 @@ moba_status_t moba_prefill_varlen(const void *q, const void *k, const void *v, v
                                   moba_dtype_t dtype, int query_chunk, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/*
+ * moba_prefill that also writes lse [batch][num_q_heads][seqlen] (fp32): for
+ * every query row the natural log of its softmax normaliser, log sum over the
+ * row's attended keys of exp(q.k / sqrt(head_dim)).  The backward pass reads
+ * it.  Errors as moba_prefill, plus INVALID_ARGUMENT for a null lse or one
+ * overlapping q or out, UNSUPPORTED for lse not 4-byte aligned.
+ */
+moba_status_t moba_prefill_lse(const void *q, const void *k, const void *v, void *out,
+                               float *lse, int batch, int seqlen, int num_q_heads,
+                               int num_kv_heads, int head_dim, int block_size, int topk,
+                               moba_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
+ * Backward pass: gradients dq, dk, dv of the attention for the upstream
+ * gradient dout, under the selection the forward made (rebuilt here from q
+ * and k: pool, gate, index, so it matches the forward's bit for bit).  The
+ * write-up trains with MoBA; the selection itself gets no gradient (the top-k
+ * is piecewise constant and the gate has no parameters).  With P the softmax
+ * weights over a row's attended keys, dP = dout . v and delta = dout . out:
+ *   dv = sum P dout,  dS = P (dP - delta),  dq = sum dS k / sqrt(d),
+ *   dk = sum dS q / sqrt(d).
+ * Inputs: q, k, v, out (the forward's output), dout as laid out above, lse
+ * from moba_prefill_lse; outputs dq like q, dk and dv like k, fully
+ * overwritten.  bf16 only: P and dS are rounded to bf16 for the matrix-core
+ * products, accumulation is fp32, dq is summed from bf16 per-block partials.
+ * Errors as moba_prefill, plus UNSUPPORTED for fp32 inputs and for topk >= n
+ * with n > 32 blocks, INVALID_ARGUMENT for any output overlapping an input or
+ * another output.  Workspace: moba_workspace_size_backward.
+ */
+moba_status_t moba_workspace_size_backward(int batch, int seqlen, int num_q_heads,
+                                           int num_kv_heads, int head_dim, int block_size,
+                                           int topk, moba_dtype_t dtype, size_t *bytes);
+moba_status_t moba_backward(const void *q, const void *k, const void *v, const void *out,
+                            const void *dout, const float *lse, void *dq, void *dk, void *dv,
+                            int batch, int seqlen, int num_q_heads, int num_kv_heads,
+                            int head_dim, int block_size, int topk, moba_dtype_t dtype,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -193,6 +193,45 @@ def test_varlen_prefill_rejects_before_any_hip_call():
     assert call([0, 640], ws=FAKE + (4 << 32) + 8) == UNS
 
 
+def test_backward_workspace_and_validation():
+    L = moba.lib()
+    nb = ctypes.c_size_t(0)
+    assert L.moba_workspace_size_backward(1, 1024, 2, 2, 64, 128, 3, BF16, ctypes.byref(nb)) == 0
+    assert nb.value > 2 * 1024 * 3 * 64 * 2                      # dq slots (bf16) and more
+    assert L.moba_workspace_size_backward(1, 1024, 2, 2, 64, 128, 3, F32, ctypes.byref(nb)) == UNS
+    assert L.moba_workspace_size_backward(1, 1024, 2, 2, 64, 128, 8, BF16, ctypes.byref(nb)) == 0
+    assert L.moba_workspace_size_backward(1, 64 * 64, 2, 2, 64, 64, 64, BF16,
+                                          ctypes.byref(nb)) == UNS   # full selection, 64 blocks
+    assert L.moba_workspace_size_backward(1, 1024, 2, 2, 64, 128, 3, BF16, None) == INV
+    vp = ctypes.c_void_p
+
+    def call(dq=FAKE + (6 << 32), q=FAKE, lse=FAKE + (5 << 32), nbytes=1 << 40, dt=BF16):
+        return L.moba_backward(vp(q), vp(FAKE + (1 << 32)), vp(FAKE + (2 << 32)),
+                               vp(FAKE + (3 << 32)), vp(FAKE + (4 << 32)), vp(lse), vp(dq),
+                               vp(FAKE + (7 << 32)), vp(FAKE + (8 << 32)), 1, 1024, 2, 2, 64, 128,
+                               3, dt, vp(FAKE + (9 << 32)), nbytes, None)
+    assert call(dq=0) == INV
+    assert call(lse=0) == INV
+    assert call(dq=FAKE + 64) == INV                             # dq overlaps q
+    assert call(dq=FAKE + (3 << 32)) == INV                      # dq overlaps out
+    assert call(q=FAKE + 8) == UNS
+    assert call(lse=FAKE + (5 << 32) + 2) == UNS
+    assert call(nbytes=1024) == WS
+    assert call(dt=F32) == UNS
+
+
+def test_prefill_lse_validation():
+    vp = ctypes.c_void_p
+
+    def call(lse):
+        return moba.lib().moba_prefill_lse(vp(FAKE), vp(FAKE + (1 << 32)), vp(FAKE + (2 << 32)),
+                                           vp(FAKE + (3 << 32)), vp(lse), 1, 1024, 2, 2, 64, 128,
+                                           3, BF16, vp(FAKE + (4 << 32)), 1 << 40, None)
+    assert call(0) == INV
+    assert call(FAKE + (5 << 32) + 2) == UNS
+    assert call(FAKE + (3 << 32) + 256) == INV                   # overlaps out
+
+
 def test_timed_prefill_needs_events():
     vp = ctypes.c_void_p
     arr = (vp * (_lib.MOBA_NUM_STAGES + 1))()
