@@ -8,6 +8,9 @@ block 4096, top-k 12).  Prints one JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-dense] [--no-cpu] [--no-secondary] [--query-chunk T]
 
+--backward times moba_backward (dq, dk, dv; the selection rebuilt inside)
+on the workload, after one moba_prefill_lse for its inputs.
+
 --workload moba-varlen-1m-gqa32x8-d128 times a packed batch of 7 sequences
 (about 1.09M tokens, every one ending in a short block) through
 moba_prefill_varlen, whole steps timed with HIP events, and the same batch
@@ -275,6 +278,66 @@ def run_varlen(moba, torch, name, dev, args):
     print(json.dumps(line), flush=True)
 
 
+def run_backward(moba, torch, cfg, dev, args):
+    """moba_backward on the workload: one JSON line (whole backward per step)."""
+    from synth import make_inputs
+    log(f"{cfg.name}: generating inputs and upstream gradient on the GPU")
+    inp = make_inputs(cfg, device=dev)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    gen = torch.Generator(device=dev).manual_seed(cfg.seed + 99)
+    dout = (torch.randn(q.shape, generator=gen, device=dev) * 0.05).to(q.dtype)
+    out, lse = moba.moba_prefill_lse(q, k, v, cfg.block_size, cfg.topk)
+    nb = moba.moba_workspace_size_backward(cfg.batch, cfg.seqlen, cfg.hq, cfg.hkv, cfg.head_dim,
+                                           cfg.block_size, cfg.topk)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    for i in range(args.warmup):
+        moba.moba_backward(q, k, v, out, dout, lse, cfg.block_size, cfg.topk, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record()
+        moba.moba_backward(q, k, v, out, dout, lse, cfg.block_size, cfg.topk, workspace=ws)
+        ev[s][1].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    ms_ev = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    # algorithmic backward work: 5 products per attended pair (QK^T again, dO V^T,
+    # P^T dO, dS K, dS^T Q), 2.5x the forward's 2
+    flops = 2.5 * work_counts(cfg)["flops_total"]
+    line = {
+        "metric": "MoBA attention backward (dq, dk, dv) tokens/s",
+        "value": cfg.batch * cfg.seqlen / (ms / 1000.0),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Gaussian Q/K/V/dO with planted high-affinity blocks)",
+        "config": {"workload": cfg.name, "pass": "backward", "batch": cfg.batch,
+                   "seq_len": cfg.seqlen, "num_q_heads": cfg.hq, "num_kv_heads": cfg.hkv,
+                   "head_dim": cfg.head_dim, "block_size": cfg.block_size, "topk": cfg.topk,
+                   "parallelism": "single-gpu"},
+        "roofline": {"kernel": "whole backward (selection rebuild, dq, dk/dv)", "bound": "mfma",
+                     "achieved": flops / (ms_ev / 1000.0) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s",
+                     "frac": flops / (ms_ev / 1000.0) / 1e12 / BF16_PEAK_TFLOPS,
+                     "traffic": None, "avg_launch_ms": round(ms_ev, 3)},
+        "backward_tflop": flops / 1e12,
+        "workspace_gb": nb / 1e9,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def time_dense(moba, torch, cfg, q, k, v):
     """Full causal attention on the same inputs (topk = number of blocks)."""
     out = torch.empty_like(q)
@@ -390,6 +453,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time moba_backward (dq, dk, dv) on the workload instead")
     ap.add_argument("--query-chunk", type=int, default=1 << 18,
                     help="query tokens per chunk for workloads generated in slices (10M)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -422,6 +487,9 @@ def main():
         run_varlen(moba, torch, args.workload, dev, args)
         return
     cfg = config_by_name(args.workload)
+    if args.backward:
+        run_backward(moba, torch, cfg, dev, args)
+        return
     if cfg.gen_slice > 0:
         run_chunked(moba, torch, cfg, dev, args)
         return

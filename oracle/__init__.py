@@ -65,7 +65,7 @@ def _load():
     lib.oracle_selection_gap.argtypes = [vp, ci, _f64p, ci, ci, ci, ci, ci, ci, ci, cll, _i64p,
                                          _i32p, _i32p, _f64p]
     lib.oracle_backward.argtypes = [vp, vp, vp, ci, _f64p, ci, ci, ci, ci, ci, ci, ci, _i32p,
-                                    _f64p, _f64p, _f64p]
+                                    ci, _f64p, _f64p, _f64p]
     for f in (lib.oracle_pool, lib.oracle_gate, lib.oracle_attend, lib.oracle_attend_merged,
               lib.oracle_selection_gap, lib.oracle_backward, lib.oracle_num_threads,
               lib.oracle_abi_version):
@@ -170,9 +170,12 @@ def attend_merged(*args):
     return _attend(_load().oracle_attend_merged, *args)
 
 
-def backward(q, k, v, code, dout, batch, S, hq, hkv, d, block, topk, idx):
+def backward(q, k, v, code, dout, batch, S, hq, hkv, d, block, topk, idx, t_lo=0):
     """Gradients (dq [b, S, hq, d], dk, dv [b, S, hkv, d], float64) of the attention under
-    the selection idx [b, hq, S, topk] for the upstream gradient dout [b, S, hq, d]."""
+    the selection idx [b, hq, S, topk] for the upstream gradient dout [b, S, hq, d].
+
+    t_lo > 0: only rows t >= t_lo are processed; dq of those rows and dk, dv of keys
+    s >= t_lo are still exact (causality), everything before is left at zero."""
     q, qp = _raw(q, code)
     k, kp = _raw(k, code)
     v, vp = _raw(v, code)
@@ -182,7 +185,7 @@ def backward(q, k, v, code, dout, batch, S, hq, hkv, d, block, topk, idx):
     dk = np.zeros((batch, S, hkv, d), dtype=np.float64)
     dv = np.zeros((batch, S, hkv, d), dtype=np.float64)
     _check(_load().oracle_backward(qp, kp, vp, code, dout, batch, S, hq, hkv, d, block, topk,
-                                   idx, dq, dk, dv), "backward")
+                                   idx, int(t_lo), dq, dk, dv), "backward")
     return dq, dk, dv
 
 

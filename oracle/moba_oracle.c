@@ -429,12 +429,15 @@ int oracle_selection_gap(const void *q, int code, const double *kbar, int batch,
  *   dq_t   = sum_s ds_ts k_s / sqrt(d),   dk_s = sum over rows of ds_ts q_t / sqrt(d)
  * idx: [batch][hq][S][topk], the layout of the GPU's block_idx.
  * dout, dq: [batch][S][hq][d]; dk, dv: [batch][S][hkv][d]; all double.
+ * Only rows t >= t_lo contribute (0: every row).  Causality makes dq of rows
+ * t >= t_lo and dk, dv of keys s >= t_lo exact all the same: no earlier row
+ * attends a later key.
  * Parallel over (batch, KV head): each owns its dk / dv rows, so no races.
  */
 int oracle_backward(const void *q, const void *k, const void *v, int code, const double *dout,
                     int batch, int S, int hq, int hkv, int d, int block, int topk,
-                    const int *idx, double *dq, double *dk, double *dv) {
-    if (!q || !k || !v || !dout || !idx || !dq || !dk || !dv) return 1;
+                    const int *idx, int t_lo, double *dq, double *dk, double *dv) {
+    if (!q || !k || !v || !dout || !idx || !dq || !dk || !dv || t_lo < 0) return 1;
     if (check_dims(batch, S, hq, hkv, d, block, topk)) return 1;
     const int n = n_blocks(S, block);
     const int group = hq / hkv;
@@ -458,7 +461,7 @@ int oracle_backward(const void *q, const void *k, const void *v, int code, const
             if (!flag || !p || !dp || !qv) continue;
             const int b = (int)(bg / hkv), g = (int)(bg % hkv);
             for (int h = g * group; h < (g + 1) * group; ++h) {
-                for (int t = 0; t < S; ++t) {
+                for (int t = t_lo; t < S; ++t) {
                     const int own = t / block;
                     const int *sel = idx + (((size_t)b * hq + h) * S + t) * topk;
                     if (mark_selection(sel, topk, own, flag, n)) {

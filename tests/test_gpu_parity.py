@@ -391,3 +391,55 @@ def test_backward_matches_oracle(cfg, dev):
     assert lse_err < 1e-2
     for name, (rl2, rmax) in errs.items():
         assert rl2 < 1e-2 and rmax < 3e-2, (name, rl2, rmax)
+
+
+@pytest.mark.timeout(400)
+def test_backward_full_size_128k(dev):
+    """The 128K workload's backward at full size: the sum rules over every key
+    of every KV head (past-block lists and own blocks alike), and every element
+    of one KV head group's dq (rows) and dk, dv (keys) in the last 512 tokens
+    against the oracle run on that group from there on (exact by causality;
+    those rows take dq from 11 past blocks, those keys dk, dv from own rows)."""
+    cfg = CONFIGS[3]
+    moba = _moba()
+    b, S, hq, hkv, d, B, topk = dims(cfg)
+    G = hq // hkv
+    log(f"case {cfg.name} backward: generating on GPU")
+    inp = make_inputs(cfg, device=dev)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    gen = torch.Generator(device=dev).manual_seed(cfg.seed + 99)
+    dout = (torch.randn((b, S, hq, d), generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+    out, lse = moba.moba_prefill_lse(q, k, v, B, topk)
+    dq, dk, dv = moba.moba_backward(q, k, v, out, dout, lse, B, topk)
+    idx = moba.moba_gate(q, k, B, topk)
+    torch.cuda.synchronize()
+    log(f"case {cfg.name} backward: GPU done")
+    # sum rules: per KV head, sum over keys of dk is 0 and of dv is sum of dout of its heads
+    dk_sum = dk.double().sum(1)                                   # [b, hkv, d]
+    dv_sum = dv.double().sum(1)
+    do_sum = dout.double().view(b, S, hkv, G, d).sum((1, 3))
+    dk_scale = dk.double().abs().sum(1)
+    rule_k = float((dk_sum.abs() / dk_scale).max())
+    rule_v = float(((dv_sum - do_sum).abs() / dv.double().abs().sum(1)).max())
+    log(f"[{cfg.name} backward] sum rules: |sum dk| / sum |dk| {rule_k:.2e}, "
+        f"|sum dv - sum dout| / sum |dv| {rule_v:.2e}")
+    assert rule_k < 1e-2 and rule_v < 1e-2
+    # one KV head group, rows and keys of the last 512 tokens
+    g = hkv - 1
+    hs = slice(g * G, (g + 1) * G)
+    t_lo = S - 512
+    host = {"q": q[:, :, hs].cpu(), "k": k[:, :, g:g + 1].cpu(), "v": v[:, :, g:g + 1].cpu()}
+    qa, ka, va, code = host_arrays(host)
+    idx_g = idx[:, hs].cpu().numpy()
+    log(f"case {cfg.name} backward: sum rules hold; oracle on rows >= {t_lo} of KV head {g}")
+    rq, rk, rv = oracle.backward(qa, ka, va, code, dout[:, :, hs].double().cpu().numpy(), b, S,
+                                 G, 1, d, B, topk, idx_g, t_lo=t_lo)
+    errs = {}
+    for name, got, ref in (("dq", dq[:, t_lo:, hs], rq[:, t_lo:]),
+                           ("dk", dk[:, t_lo:, g:g + 1], rk[:, t_lo:]),
+                           ("dv", dv[:, t_lo:, g:g + 1], rv[:, t_lo:])):
+        gg = got.double().cpu().numpy()
+        errs[name] = (_rel_l2(gg, ref), float(np.abs(gg - ref).max() / np.abs(ref).max()))
+    log(f"[{cfg.name} backward] (rel L2, max-abs / max|ref|) {errs}")
+    for name, (rl2, rmax) in errs.items():
+        assert rl2 < 1e-2 and rmax < 3e-2, (name, rl2, rmax)

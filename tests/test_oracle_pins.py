@@ -445,3 +445,20 @@ def test_backward_sum_rules():
                                    rtol=1e-10, atol=1e-10)
         np.testing.assert_allclose(dk[0, :, g].sum(0), 0.0, atol=1e-10)
     assert np.abs(dq).max() > 1e-3 and np.abs(dk).max() > 1e-3
+
+
+def test_backward_row_range_is_exact_past_t_lo():
+    """Pin: with rows restricted to t >= t_lo, dq of those rows and dk, dv of
+    keys >= t_lo equal the full computation (no earlier row sees a later key),
+    while the skipped rows' dq stays zero."""
+    S, hq, hkv, d, block, topk = 96, 4, 2, 8, 16, 3
+    q, k, v = rand_inputs(S, hq, hkv, d, seed=8, planted=1, block=block)
+    dout = np.random.default_rng(4).standard_normal((1, S, hq, d))
+    idx = _selection(q, k, block, topk)
+    full = oracle.backward(q, k, v, 1, dout, 1, S, hq, hkv, d, block, topk, idx)
+    t_lo = 64
+    part = oracle.backward(q, k, v, 1, dout, 1, S, hq, hkv, d, block, topk, idx, t_lo=t_lo)
+    for f, p in zip(full, part):
+        np.testing.assert_allclose(p[:, t_lo:], f[:, t_lo:], rtol=1e-12, atol=1e-14)
+    assert np.all(part[0][:, :t_lo] == 0.0)
+    assert np.abs(full[1][:, :t_lo] - part[1][:, :t_lo]).max() > 1e-6   # earlier keys differ
