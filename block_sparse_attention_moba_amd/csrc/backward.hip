@@ -19,10 +19,11 @@
 //                     256 rows over the block's keys and writes one partial
 //                     slot per (row, block), like the forward's partial outputs.
 //   bwd_dq_sum_kernel the row's partial slots added up (fixed order) into dq.
-//   bwd_dkdv_kernel   one workgroup per (batch, KV head, block, 128 keys): it
+//   bwd_kv_kernel     one workgroup per (batch, KV head, block, 256 keys): it
 //                     walks every query row that attends these keys (the
 //                     block's list, then the block's own rows, causal) and owns
-//                     dK and dV of its keys, so no atomics and no reduction.
+//                     dV (first pass) or dK (second pass) of its keys, so no
+//                     atomics and no reduction.
 #include "moba_internal.hpp"
 
 namespace moba {
@@ -314,26 +315,40 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const __bf16 *__restric
 
 // ---------------------------------------------------------------- dk, dv
 
-constexpr int kKeysPerWG = 128;   // 4 waves x 32 keys
+constexpr int kKeysPerWG = 256;   // 8 waves x 32 keys
+constexpr int kKvDepth = 2;       // row chunks in flight: the one in LDS and 1 loading
+enum KvPass { kPassDV = 0, kPassDK = 1 };
 
-// grid (ceil(B / 128), n, batch * Hkv), 256 threads.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+// One pass over the query rows that attend a workgroup's 256 keys: the
+// block's list (past rows, every key visible), then the block's own rows
+// t >= k0 of every head of the group (causal).  PASS dV: S, P, dV^T += dO^T P.
+// PASS dK: S, dP, dS, dK^T += Q^T dS.  Two passes instead of one keep each
+// under 256 registers, so two waves share a SIMD (one pass holding both
+// accumulators and both operands needs one SIMD per wave); S is computed twice.
+// grid: (ceil(B / 256) key groups x n blocks x batch * Hkv, rounded up to a
+// multiple of 8), 512 threads.  Consecutive workgroups -- the key groups of one
+// block's list, which read the same query rows -- run on the same XCD.
+template <int D, int PASS>
+__global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsigned nwg) {
     __shared__ __attribute__((aligned(16))) __bf16 sQ[kBS * D];
     __shared__ __attribute__((aligned(16))) __bf16 sG[kBS * D];
     __shared__ __attribute__((aligned(16))) float sL[kBS];
     __shared__ __attribute__((aligned(16))) float sD[kBS];
     __shared__ __attribute__((aligned(16))) int sT[kBS];
     constexpr int CPR = D / 8;
-    const int j = blockIdx.y;
-    const int b = blockIdx.z / a.Hkv, g = blockIdx.z % a.Hkv;
+    const unsigned wg = xcd_tile(blockIdx.x, gridDim.x);
+    if (wg >= nwg) return;
+    const int sub = (int)(wg % nsub);
+    const int j = (int)((wg / nsub) % a.n);
+    const int bg = (int)(wg / ((unsigned)nsub * a.n));
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int blk_end = min((j + 1) * a.B, a.S);
-    const int k0 = j * a.B + blockIdx.x * kKeysPerWG;
+    const int k0 = j * a.B + sub * kKeysPerWG;
     if (k0 >= blk_end) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, half = lane >> 5;
 
-    // this lane's key (matrix-core column) and its K, V operands
+    // this lane's key (matrix-core column) and its K (and V) operands
     const int key = k0 + wave * 32 + col;
     const bool kvalid = key < blk_end;
     const size_t rstride = (size_t)a.Hkv * D;
@@ -342,11 +357,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
         kf[kk] = *reinterpret_cast<const bf16x8_t *>(a.k + koff + kk * 16);
-        vf[kk] = *reinterpret_cast<const bf16x8_t *>(a.v + koff + kk * 16);
+        if (PASS == kPassDK) vf[kk] = *reinterpret_cast<const bf16x8_t *>(a.v + koff + kk * 16);
     }
 
-    // query rows: the block's list (past rows, every key visible), then the
-    // block's own rows t >= k0 of every head of the group (causal)
     const long long lid = ((long long)b * a.Hkv + g) * a.n + j;
     const uint64_t lbeg = a.list_off[lid];
     const long long nlist = (long long)(a.list_off[lid + 1] - lbeg);
@@ -355,11 +368,12 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const int cph = (own_rows + kBS - 1) / kBS;      // own chunks per head
     const int nc = nc1 + cph * a.G;
 
-    // staging: thread -> (row, chunk) pieces of the Q and dO rows of a chunk
-    constexpr int PPT = kBS * CPR / 256;            // 16-byte pieces per thread
-    uint4 qn[PPT], gn[PPT];
-    float ln = INFINITY, dn = 0.f;
-    int tn = -1;
+    // staging: thread -> one (row, chunk) piece of the Q and dO rows of a chunk
+    const int srr = tid / CPR, scc = tid % CPR;
+    const bool stager = tid < kBS * CPR;
+    uint4 qn[kKvDepth], gn[kKvDepth];
+    float ln[kKvDepth], dn[kKvDepth];
+    int tn[kKvDepth];
     auto row_of = [&](int ci, int rr, int &t, int &h) -> bool {
         if (ci < nc1) {
             const long long e = (long long)ci * kBS + rr;
@@ -374,119 +388,118 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         h = g * a.G + c2 / cph;
         return t < blk_end;
     };
-    auto fetch = [&](int ci) {
-#pragma unroll
-        for (int p = 0; p < PPT; ++p) {
-            const int e = p * 256 + tid, rr = e / CPR, cc = e % CPR;
+    auto fetch = [&](int ci, int u) {
+        if (stager) {
             int t = 0, h = 0;
-            if (row_of(ci, rr, t, h)) {
-                const size_t o = (((size_t)b * a.S + t) * a.Hq + h) * D + cc * 8;
-                qn[p] = *reinterpret_cast<const uint4 *>(a.q + o);
-                gn[p] = *reinterpret_cast<const uint4 *>(a.dout + o);
+            if (row_of(ci, srr, t, h)) {
+                const size_t o = (((size_t)b * a.S + t) * a.Hq + h) * D + scc * 8;
+                qn[u] = *reinterpret_cast<const uint4 *>(a.q + o);
+                gn[u] = *reinterpret_cast<const uint4 *>(a.dout + o);
             } else {
-                qn[p] = make_uint4(0, 0, 0, 0);
-                gn[p] = make_uint4(0, 0, 0, 0);
+                qn[u] = make_uint4(0, 0, 0, 0);
+                gn[u] = make_uint4(0, 0, 0, 0);
             }
         }
         if (tid < kBS) {
             int t = 0, h = 0;
             if (row_of(ci, tid, t, h)) {
                 const size_t rid = ((size_t)b * a.Hq + h) * a.S + t;
-                ln = a.l2[rid];
-                dn = a.delta[rid];
-                tn = ci < nc1 ? 0x7fffffff : t;      // past rows see every key
+                ln[u] = a.l2[rid];
+                dn[u] = a.delta[rid];
+                tn[u] = ci < nc1 ? 0x7fffffff : t;      // past rows see every key
             } else {
-                ln = INFINITY;
-                dn = 0.f;
-                tn = -1;
+                ln[u] = INFINITY;
+                dn[u] = 0.f;
+                tn[u] = -1;
             }
         }
     };
-    auto store = [&]() {
-#pragma unroll
-        for (int p = 0; p < PPT; ++p) {
-            const int e = p * 256 + tid, rr = e / CPR, cc = e % CPR;
-            *reinterpret_cast<uint4 *>(&sQ[lds_off<D>(rr, cc)]) = qn[p];
-            *reinterpret_cast<uint4 *>(&sG[lds_off<D>(rr, cc)]) = gn[p];
+    auto store = [&](int u) {
+        if (stager) {
+            *reinterpret_cast<uint4 *>(&sQ[lds_off<D>(srr, scc)]) = qn[u];
+            *reinterpret_cast<uint4 *>(&sG[lds_off<D>(srr, scc)]) = gn[u];
         }
         if (tid < kBS) {
-            sL[tid] = ln;
-            sD[tid] = dn;
-            sT[tid] = tn;
+            sL[tid] = ln[u];
+            sD[tid] = dn[u];
+            sT[tid] = tn[u];
         }
     };
 
-    f32x16_t dk[D / 32], dv[D / 32];
+    f32x16_t acc[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dk[dt][i] = dv[dt][i] = 0.f;
+        for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
     const f32x16_t zero16 = {};
-    if (nc > 0) fetch(0);
-    for (int ci = 0; ci < nc; ++ci) {
-        store();
+#pragma unroll
+    for (int u = 0; u < kKvDepth - 1; ++u)
+        if (u < nc) fetch(u, u);
+    for (int c2 = 0; c2 < nc; c2 += kKvDepth)
+#pragma unroll
+    for (int u = 0; u < kKvDepth; ++u) {
+        const int ci = c2 + u;
+        if (ci >= nc) break;
+        store(u);
         __syncthreads();
-        if (ci + 1 < nc) fetch(ci + 1);
-        // S = Q K^T and dP = dO V^T: rows = 32 query rows, columns = this wave's keys
+        if (ci + kKvDepth - 1 < nc) fetch(ci + kKvDepth - 1, (u + kKvDepth - 1) % kKvDepth);
+        // S = Q K^T (and dP = dO V^T): rows = 32 query rows, columns = this wave's keys
         f32x16_t s = zero16, dp = zero16;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(sQ, col, kk, half), kf[kk], s,
                                                         0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(sG, col, kk, half), vf[kk],
-                                                         dp, 0, 0, 0);
+            if (PASS == kPassDK)
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(sG, col, kk, half),
+                                                             vf[kk], dp, 0, 0, 0);
         }
         // register i holds row 8 (i / 4) + 4 half + i % 4
-        float p[16], ds[16];
+        float w[16];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const int r0 = 8 * i4 + 4 * half;
             const float4 l4 = *reinterpret_cast<const float4 *>(&sL[r0]);
-            const float4 d4 = *reinterpret_cast<const float4 *>(&sD[r0]);
             const int4 t4 = *reinterpret_cast<const int4 *>(&sT[r0]);
             const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
             const int tv[4] = {t4.x, t4.y, t4.z, t4.w};
+            float dvv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (PASS == kPassDK) {
+                const float4 d4 = *reinterpret_cast<const float4 *>(&sD[r0]);
+                dvv[0] = d4.x; dvv[1] = d4.y; dvv[2] = d4.z; dvv[3] = d4.w;
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 4 * i4 + e;
                 float pe = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lv[e]));
                 if (!kvalid || key > tv[e]) pe = 0.f;
-                p[i] = pe;
-                ds[i] = pe * (dp[i] - dvv[e]);
+                w[i] = PASS == kPassDV ? pe : pe * (dp[i] - dvv[e]);
             }
         }
-        bf16x8_t pb[2], db[2];
-        pack16(p, pb);
-        pack16(ds, db);
-        // dV^T += dO^T P and dK^T += Q^T dS over the chunk's 32 rows
+        bf16x8_t wb[2];
+        pack16(w, wb);
+        // dV^T += dO^T P, or dK^T += Q^T dS, over the chunk's 32 rows
+        const __bf16 *src = PASS == kPassDV ? sG : sQ;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sG, h2, dt, lane),
-                                                                 pb[h2], dv[dt], 0, 0, 0);
-                dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(sQ, h2, dt, lane),
-                                                                 db[h2], dk[dt], 0, 0, 0);
-            }
+            for (int dt = 0; dt < D / 32; ++dt)
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(src, h2, dt, lane),
+                                                                  wb[h2], acc[dt], 0, 0, 0);
         __syncthreads();
     }
     if (!kvalid) return;
     // lane (key, half) holds dims dt * 32 + 8 (i / 4) + 4 half + i % 4
-    const size_t o = ((size_t)b * a.S + key) * rstride + (size_t)g * D;
+    __bf16 *dst = (PASS == kPassDV ? a.dv : a.dk) + ((size_t)b * a.S + key) * rstride +
+                  (size_t)g * D;
+    const float f = PASS == kPassDV ? 1.f : a.scale;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-            bf16x4_t wk, wv;
+            bf16x4_t o;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                wk[e] = (__bf16)(dk[dt][4 * i4 + e] * a.scale);
-                wv[e] = (__bf16)dv[dt][4 * i4 + e];
-            }
-            const int d = dt * 32 + 8 * i4 + 4 * half;
-            *reinterpret_cast<bf16x4_t *>(a.dk + o + d) = wk;
-            *reinterpret_cast<bf16x4_t *>(a.dv + o + d) = wv;
+            for (int e = 0; e < 4; ++e) o[e] = (__bf16)(acc[dt][4 * i4 + e] * f);
+            *reinterpret_cast<bf16x4_t *>(dst + dt * 32 + 8 * i4 + 4 * half) = o;
         }
 }
 
@@ -527,8 +540,10 @@ hipError_t backward_impl(const BwdBuffers &bb, const Problem &p, uint64_t tiles_
     bwd_dq_kernel<D, kOwnTile><<<(a.ntiles + 7) / 8 * 8, 512, 0, st>>>(a);
     bwd_dq_sum_kernel<D><<<rgrid, 256, 0, st>>>(a.part_dq, static_cast<__bf16 *>(bb.dq), p.S,
                                                 p.Hq, p.B, p.topk, a.nslot, rows);
-    dim3 kgrid((p.B + kKeysPerWG - 1) / kKeysPerWG, p.n, p.batch * p.Hkv);
-    bwd_dkdv_kernel<D><<<kgrid, 256, 0, st>>>(a);
+    const int nsub = (p.B + kKeysPerWG - 1) / kKeysPerWG;
+    const unsigned nwg = (unsigned)(nsub * p.n * p.batch * p.Hkv);
+    bwd_kv_kernel<D, kPassDV><<<(nwg + 7) / 8 * 8, 512, 0, st>>>(a, nsub, nwg);
+    bwd_kv_kernel<D, kPassDK><<<(nwg + 7) / 8 * 8, 512, 0, st>>>(a, nsub, nwg);
     return hipGetLastError();
 }
 
