@@ -316,7 +316,6 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const __bf16 *__restric
 // ---------------------------------------------------------------- dk, dv
 
 constexpr int kKeysPerWG = 256;   // 8 waves x 32 keys
-constexpr int kKvDepth = 2;       // row chunks in flight: the one in LDS and 1 loading
 enum KvPass { kPassDV = 0, kPassDK = 1 };
 
 // One pass over the query rows that attend a workgroup's 256 keys: the
@@ -330,11 +329,12 @@ enum KvPass { kPassDV = 0, kPassDK = 1 };
 // block's list, which read the same query rows -- run on the same XCD.
 template <int D, int PASS>
 __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsigned nwg) {
-    __shared__ __attribute__((aligned(16))) __bf16 sQ[kBS * D];
-    __shared__ __attribute__((aligned(16))) __bf16 sG[kBS * D];
-    __shared__ __attribute__((aligned(16))) float sL[kBS];
-    __shared__ __attribute__((aligned(16))) float sD[kBS];
-    __shared__ __attribute__((aligned(16))) int sT[kBS];
+    // two chunk buffers: chunk c + 1 is stored while others still read chunk c
+    __shared__ __attribute__((aligned(16))) __bf16 sQ[2][kBS * D];
+    __shared__ __attribute__((aligned(16))) __bf16 sG[2][kBS * D];
+    __shared__ __attribute__((aligned(16))) float sL[2][kBS];
+    __shared__ __attribute__((aligned(16))) float sD[2][kBS];
+    __shared__ __attribute__((aligned(16))) int sT[2][kBS];
     constexpr int CPR = D / 8;
     const unsigned wg = xcd_tile(blockIdx.x, gridDim.x);
     if (wg >= nwg) return;
@@ -371,9 +371,9 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
     // staging: thread -> one (row, chunk) piece of the Q and dO rows of a chunk
     const int srr = tid / CPR, scc = tid % CPR;
     const bool stager = tid < kBS * CPR;
-    uint4 qn[kKvDepth], gn[kKvDepth];
-    float ln[kKvDepth], dn[kKvDepth];
-    int tn[kKvDepth];
+    uint4 qn = {}, gn = {};
+    float ln = INFINITY, dn = 0.f;
+    int tn = -1;
     auto row_of = [&](int ci, int rr, int &t, int &h) -> bool {
         if (ci < nc1) {
             const long long e = (long long)ci * kBS + rr;
@@ -388,41 +388,41 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
         h = g * a.G + c2 / cph;
         return t < blk_end;
     };
-    auto fetch = [&](int ci, int u) {
+    auto fetch = [&](int ci) {
         if (stager) {
             int t = 0, h = 0;
             if (row_of(ci, srr, t, h)) {
                 const size_t o = (((size_t)b * a.S + t) * a.Hq + h) * D + scc * 8;
-                qn[u] = *reinterpret_cast<const uint4 *>(a.q + o);
-                gn[u] = *reinterpret_cast<const uint4 *>(a.dout + o);
+                qn = *reinterpret_cast<const uint4 *>(a.q + o);
+                gn = *reinterpret_cast<const uint4 *>(a.dout + o);
             } else {
-                qn[u] = make_uint4(0, 0, 0, 0);
-                gn[u] = make_uint4(0, 0, 0, 0);
+                qn = make_uint4(0, 0, 0, 0);
+                gn = make_uint4(0, 0, 0, 0);
             }
         }
         if (tid < kBS) {
             int t = 0, h = 0;
             if (row_of(ci, tid, t, h)) {
                 const size_t rid = ((size_t)b * a.Hq + h) * a.S + t;
-                ln[u] = a.l2[rid];
-                dn[u] = a.delta[rid];
-                tn[u] = ci < nc1 ? 0x7fffffff : t;      // past rows see every key
+                ln = a.l2[rid];
+                dn = a.delta[rid];
+                tn = ci < nc1 ? 0x7fffffff : t;      // past rows see every key
             } else {
-                ln[u] = INFINITY;
-                dn[u] = 0.f;
-                tn[u] = -1;
+                ln = INFINITY;
+                dn = 0.f;
+                tn = -1;
             }
         }
     };
-    auto store = [&](int u) {
+    auto store = [&](int buf) {
         if (stager) {
-            *reinterpret_cast<uint4 *>(&sQ[lds_off<D>(srr, scc)]) = qn[u];
-            *reinterpret_cast<uint4 *>(&sG[lds_off<D>(srr, scc)]) = gn[u];
+            *reinterpret_cast<uint4 *>(&sQ[buf][lds_off<D>(srr, scc)]) = qn;
+            *reinterpret_cast<uint4 *>(&sG[buf][lds_off<D>(srr, scc)]) = gn;
         }
         if (tid < kBS) {
-            sL[tid] = ln[u];
-            sD[tid] = dn[u];
-            sT[tid] = tn[u];
+            sL[buf][tid] = ln;
+            sD[buf][tid] = dn;
+            sT[buf][tid] = tn;
         }
     };
 
@@ -432,25 +432,26 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
     const f32x16_t zero16 = {};
+    if (nc > 0) {
+        fetch(0);
+        store(0);
+    }
+    __syncthreads();
+    for (int c2 = 0; c2 < nc; c2 += 2)
 #pragma unroll
-    for (int u = 0; u < kKvDepth - 1; ++u)
-        if (u < nc) fetch(u, u);
-    for (int c2 = 0; c2 < nc; c2 += kKvDepth)
-#pragma unroll
-    for (int u = 0; u < kKvDepth; ++u) {
-        const int ci = c2 + u;
+    for (int buf = 0; buf < 2; ++buf) {
+        const int ci = c2 + buf;
         if (ci >= nc) break;
-        store(u);
-        __syncthreads();
-        if (ci + kKvDepth - 1 < nc) fetch(ci + kKvDepth - 1, (u + kKvDepth - 1) % kKvDepth);
+        if (ci + 1 < nc) fetch(ci + 1);
+        const __bf16 *sq = sQ[buf], *sg = sG[buf];
         // S = Q K^T (and dP = dO V^T): rows = 32 query rows, columns = this wave's keys
         f32x16_t s = zero16, dp = zero16;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(sQ, col, kk, half), kf[kk], s,
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(sq, col, kk, half), kf[kk], s,
                                                         0, 0, 0);
             if (PASS == kPassDK)
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(sG, col, kk, half),
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(sg, col, kk, half),
                                                              vf[kk], dp, 0, 0, 0);
         }
         // register i holds row 8 (i / 4) + 4 half + i % 4
@@ -458,13 +459,13 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             const int r0 = 8 * i4 + 4 * half;
-            const float4 l4 = *reinterpret_cast<const float4 *>(&sL[r0]);
-            const int4 t4 = *reinterpret_cast<const int4 *>(&sT[r0]);
+            const float4 l4 = *reinterpret_cast<const float4 *>(&sL[buf][r0]);
+            const int4 t4 = *reinterpret_cast<const int4 *>(&sT[buf][r0]);
             const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
             const int tv[4] = {t4.x, t4.y, t4.z, t4.w};
             float dvv[4] = {0.f, 0.f, 0.f, 0.f};
             if (PASS == kPassDK) {
-                const float4 d4 = *reinterpret_cast<const float4 *>(&sD[r0]);
+                const float4 d4 = *reinterpret_cast<const float4 *>(&sD[buf][r0]);
                 dvv[0] = d4.x; dvv[1] = d4.y; dvv[2] = d4.z; dvv[3] = d4.w;
             }
 #pragma unroll
@@ -478,13 +479,15 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
         bf16x8_t wb[2];
         pack16(w, wb);
         // dV^T += dO^T P, or dK^T += Q^T dS, over the chunk's 32 rows
-        const __bf16 *src = PASS == kPassDV ? sG : sQ;
+        const __bf16 *src = PASS == kPassDV ? sg : sq;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(src, h2, dt, lane),
                                                                   wb[h2], acc[dt], 0, 0, 0);
+        // the other buffer was last read before the previous barrier
+        if (ci + 1 < nc) store(buf ^ 1);
         __syncthreads();
     }
     if (!kvalid) return;
