@@ -18,7 +18,7 @@ constexpr long long kMaxSeq = 1ll << 24;
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-    size_t kbar = 0, kmax2 = 0, khl = 0, poolp = 0, pooln = 0, defer = 0, idx = 0, cnt = 0, cursor = 0,
+    size_t kbar = 0, kmax2 = 0, khl = 0, defer = 0, idx = 0, cnt = 0, cursor = 0,
            list_off = 0, tile_off = 0, tile_list = 0, lists = 0, part_o = 0, part_lse = 0,
            l2 = 0, delta = 0, part_dq = 0, total = 0;
 };
@@ -92,13 +92,10 @@ ChunkBound chunk_bound(const Problem &p, int C) {
 Layout gate_layout(const Problem &p) {
     Layout l;
     size_t off = 0;
-    const size_t nchunk = p.B / pool_chunk(p.B);
     const size_t blocks = (size_t)p.batch * p.Hkv * p.n;
     l.kbar = off; off += align_up(blocks * p.D * 4);
     l.kmax2 = off; off += align_up(blocks * 4);
     l.khl = off; off += align_up(blocks * 2 * p.D * 2);
-    l.poolp = off; off += align_up(blocks * nchunk * p.D * 4);
-    l.pooln = off; off += align_up(blocks * nchunk * 4);
     l.total = off;
     return l;
 }
@@ -186,8 +183,6 @@ PoolBuffers pool_buffers(char *w, const Layout &l, float *kbar_out) {
     pb.kbar = kbar_out ? kbar_out : reinterpret_cast<float *>(w + l.kbar);
     pb.kmax2 = reinterpret_cast<float *>(w + l.kmax2);
     pb.khl = reinterpret_cast<__bf16 *>(w + l.khl);
-    pb.partial = reinterpret_cast<float *>(w + l.poolp);
-    pb.partial_nmax = reinterpret_cast<float *>(w + l.pooln);
     return pb;
 }
 

@@ -49,8 +49,6 @@ struct PoolBuffers {
     float *kbar;           // [batch][Hkv][n][D] block means
     float *kmax2;          // [batch][Hkv][n] largest squared key norm of each block
     __bf16 *khl;           // [batch][Hkv][n][2][D] bf16 split of the means: hi = rne(x), lo = rne(x - hi)
-    float *partial;        // [batch][Hkv][n][chunks][D] chunk sums
-    float *partial_nmax;   // [batch][Hkv][n][chunks] chunk norm maxima
 };
 hipError_t launch_pool(const void *k, const PoolBuffers &pb, const Problem &p, hipStream_t st);
 hipError_t launch_gate(const void *q, const float *kbar, const __bf16 *khl, int32_t *idx,
@@ -115,7 +113,5 @@ inline int part_slots(const Problem &p) { return p.topk; }
 // Backward dq slots per row: past blocks, then the own block (slot - 1).
 inline int bwd_slots(const Problem &p) { return p.topk < p.n ? p.topk : p.n; }
 
-// Pool partial-sum chunk length (tokens) for a block size that is a multiple of 64.
-inline int pool_chunk(int B) { return (B % 256 == 0) ? 256 : (B % 128 == 0 ? 128 : 64); }
 
 }  // namespace moba

@@ -2,15 +2,16 @@
 // the gate compares each query with; Taiwan AI overview of MoBA, section
 // "技術細節與優勢").
 //
-// Two launches.  pool_partial: one workgroup per (chunk of CT tokens, block,
-// KV head, batch) streams CT x D keys with 16-byte loads (one D-row per
-// D/8 lanes, so a wave reads 64 x 16 contiguous bytes per step) and writes
-// the chunk's fp32 column sums and the largest squared key norm of the chunk.
-// pool_finalize: sums the chunk partials of a block in a fixed order and
-// divides by the block's token count (B, or S mod B for a short last block), writes the mean also as a bf16 hi + lo pair (the
-// operands of the matrix-core gate), and takes the block's largest squared key
-// norm (the attention kernels bound every logit of the block by it).  No atomics,
-// so the result is bitwise reproducible.
+// One launch, one workgroup of 1024 threads per (block, KV head, batch): it
+// streams the block's B x D keys with 16-byte loads (one D-row per D/8 lanes,
+// eight loads in flight per thread), adds them up in a fixed order (per
+// thread, then across the rows of a pass through LDS), divides by the tokens
+// present (B, or S mod B for a short last block), and writes the mean in fp32
+// and as a bf16 hi + lo pair (the operands of the matrix-core gate), with the
+// block's largest squared key norm (the attention kernels bound every logit of
+// the block by it).  No atomics, so the result is bitwise reproducible.
+#include <type_traits>
+
 #include "moba_internal.hpp"
 
 namespace moba {
@@ -32,101 +33,102 @@ __device__ inline void load8(const float *p, float *f) {
     f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// grid (nchunk, n * Hkv, batch), 256 threads.
+// Sum over each aligned group of N lanes (N = 8 or 16), the result in every
+// lane of the group, by DPP moves instead of LDS permutes: swap neighbours,
+// swap pairs, mirror within 8 lanes, mirror within 16 lanes.
+template <int N>
+__device__ inline float group_sum(float x) {
+    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    auto dpp = [](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), decltype(ctrl)::value,
+                                                       0xF, 0xF, false));
+    };
+    x += dpp(x, std::integral_constant<int, 0xB1>{});    // quad_perm [1, 0, 3, 2]
+    x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2, 3, 0, 1]
+    x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+    if constexpr (N == 16) x += dpp(x, std::integral_constant<int, 0x140>{});   // row_mirror
+    return x;
+}
+
+constexpr int kPoolThreads = 1024;
+constexpr int kPoolUnroll = 8;
+
+// grid (n * Hkv, batch), 1024 threads.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_partial_kernel(const T *__restrict__ k,
-                                                           float *__restrict__ partial,
-                                                           float *__restrict__ partial_nmax, int S,
-                                                           int Hkv, int B, int n, int CT) {
-    constexpr int LPT = D / 8;       // lanes per token row
-    constexpr int TPP = 256 / LPT;   // token rows per pass
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(const T *__restrict__ k,
+                                                            float *__restrict__ kbar,
+                                                            float *__restrict__ kmax2,
+                                                            __bf16 *__restrict__ khl, int S,
+                                                            int Hkv, int B, int n) {
+    constexpr int LPT = D / 8;                  // lanes per token row
+    constexpr int TPP = kPoolThreads / LPT;     // token rows per pass
     __shared__ float red[TPP][D + 1];
     __shared__ float redn[TPP];
-    const int chunk = blockIdx.x;
-    const int j = blockIdx.y / Hkv;
-    const int g = blockIdx.y % Hkv;
-    const int b = blockIdx.z;
+    const int j = blockIdx.x / Hkv;
+    const int g = blockIdx.x % Hkv;
+    const int b = blockIdx.y;
     const int tid = threadIdx.x;
     const int vec = tid % LPT;
     const int tr = tid / LPT;
+    const int t0 = j * B;
+    const int t1 = min(t0 + B, S);              // a short last block ends at S
+    const size_t rstride = (size_t)Hkv * D;
+    const T *base = k + ((size_t)b * S * Hkv + g) * D + vec * 8;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     float nmax = 0.f;
-    const int t0 = j * B + chunk * CT;
-    const int t1 = min(t0 + CT, S);              // a short last block ends at S
-    for (int t = t0 + tr; t < t1; t += TPP) {
-        float f[8];
-        load8(k + (((size_t)b * S + t) * Hkv + g) * D + vec * 8, f);
-        float sq = 0.f;
+    for (int t = t0 + tr; t < t1; t += TPP * kPoolUnroll) {
+        // all loads issued before any is used: rows past the block end read its
+        // last row (in bounds) and are zeroed afterwards, so no load sits in a branch
+        float f[kPoolUnroll][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            acc[e] += f[e];
-            sq = fmaf(f[e], f[e], sq);
+        for (int u = 0; u < kPoolUnroll; ++u)
+            load8(base + (size_t)min(t + u * TPP, t1 - 1) * rstride, f[u]);
+#pragma unroll
+        for (int u = 0; u < kPoolUnroll; ++u)
+            if (t + u * TPP >= t1)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[u][e] = 0.f;
+#pragma unroll
+        for (int u = 0; u < kPoolUnroll; ++u) {
+            float sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                acc[e] += f[u][e];
+                sq = fmaf(f[u][e], f[u][e], sq);
+            }
+            // squared norm of the token: sum over the LPT lanes that hold its row
+            nmax = fmaxf(nmax, group_sum<LPT>(sq));
         }
-        // squared norm of token t: sum over the LPT lanes that hold its row
-#pragma unroll
-        for (int off = 1; off < LPT; off <<= 1) sq += __shfl_xor(sq, off, LPT);
-        nmax = fmaxf(nmax, sq);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[tr][vec * 8 + e] = acc[e];
     if (vec == 0) redn[tr] = nmax;
     __syncthreads();
-    const int nchunk = gridDim.x;
-    const size_t pc = (((size_t)b * Hkv + g) * n + j) * nchunk + chunk;
+    const size_t blk = ((size_t)b * Hkv + g) * n + j;
     if (tid < D) {
-        float s = 0.f;
-        for (int r = 0; r < TPP; ++r) s += red[r][tid];
-        partial[pc * D + tid] = s;
-    }
-    if (tid == 0) {
-        float m = 0.f;
-        for (int r = 0; r < TPP; ++r) m = fmaxf(m, redn[r]);
-        partial_nmax[pc] = m;
-    }
-}
-
-// grid (ceil(batch * Hkv * n * D / 256)), 256 threads: one output element each.
-__global__ __launch_bounds__(256) void pool_finalize_kernel(const float *__restrict__ partial,
-                                                            const float *__restrict__ partial_nmax,
-                                                            float *__restrict__ kbar,
-                                                            float *__restrict__ kmax2,
-                                                            __bf16 *__restrict__ khl,
-                                                            long long total, int D, int nchunk,
-                                                            int B, int S, int n) {
-    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (e >= total) return;
-    const long long blk = e / D;
-    const int i = (int)(e % D);
-    const float *src = partial + (size_t)blk * nchunk * D + i;
-    float s = 0.f;
-    for (int c = 0; c < nchunk; ++c) s += src[(size_t)c * D];
-    const int j = (int)(blk % n);
-    const float m = s / (float)min(B, S - j * B);   // tokens present in block j
-    kbar[e] = m;
-    // bf16 split for the matrix-core gate: m = hi + lo + O(2^-17 |m|)
-    const __bf16 hi = (__bf16)m;
-    khl[(blk * 2) * D + i] = hi;
-    khl[(blk * 2 + 1) * D + i] = (__bf16)(m - (float)hi);
-    if (i == 0) {
-        float m = 0.f;
-        for (int c = 0; c < nchunk; ++c) m = fmaxf(m, partial_nmax[(size_t)blk * nchunk + c]);
-        kmax2[blk] = m;
+        float sum = 0.f;
+        for (int r = 0; r < TPP; ++r) sum += red[r][tid];
+        const float m = sum / (float)(t1 - t0);
+        kbar[blk * D + tid] = m;
+        // bf16 split for the matrix-core gate: m = hi + lo + O(2^-17 |m|)
+        const __bf16 hi = (__bf16)m;
+        khl[(blk * 2) * D + tid] = hi;
+        khl[(blk * 2 + 1) * D + tid] = (__bf16)(m - (float)hi);
+    } else if (tid == D) {
+        float mx = 0.f;
+        for (int r = 0; r < TPP; ++r) mx = fmaxf(mx, redn[r]);
+        kmax2[blk] = mx;
     }
 }
 
 template <typename T, int D>
 static hipError_t pool_impl(const void *k, const PoolBuffers &pb, const Problem &p,
                             hipStream_t st) {
-    const int CT = pool_chunk(p.B);
-    const int nchunk = p.B / CT;
-    dim3 grid(nchunk, p.n * p.Hkv, p.batch);
-    pool_partial_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T *>(k), pb.partial,
-                                                    pb.partial_nmax, p.S, p.Hkv, p.B, p.n, CT);
-    const long long total = (long long)p.batch * p.Hkv * p.n * D;
-    pool_finalize_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(
-        pb.partial, pb.partial_nmax, pb.kbar, pb.kmax2, pb.khl, total, D, nchunk, p.B, p.S, p.n);
+    dim3 grid(p.n * p.Hkv, p.batch);
+    pool_kernel<T, D><<<grid, kPoolThreads, 0, st>>>(static_cast<const T *>(k), pb.kbar, pb.kmax2,
+                                                     pb.khl, p.S, p.Hkv, p.B, p.n);
     return hipGetLastError();
 }
 
