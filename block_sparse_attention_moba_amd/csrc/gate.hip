@@ -125,21 +125,6 @@ __global__ __launch_bounds__(256) void gate_kernel(const T *__restrict__ q,
 
 constexpr int kGateMaxWaves = 8;
 
-// Insert (cs, cj) into the sorted list: strictly higher scores displace.
-template <int KP>
-__device__ __forceinline__ void list_insert(float (&val)[KP], int (&ix)[KP], float cs, int cj) {
-#pragma unroll
-    for (int p = 0; p < KP; ++p) {
-        const bool c = cs > val[p];
-        const float tv = val[p];
-        const int ti = ix[p];
-        val[p] = c ? cs : tv;
-        ix[p] = c ? cj : ti;
-        cs = c ? tv : cs;
-        cj = c ? ti : cj;
-    }
-}
-
 // Spread the 4 nibbles of a 16-bit value to the even nibbles of a 32-bit word.
 __device__ inline uint32_t spread_nibbles(uint32_t x) {
     x &= 0xffffu;
@@ -159,16 +144,16 @@ __device__ __forceinline__ void value_insert(float (&val)[KP], float x) {
 // grid (ceil(S / (32 TW)), Hkv, batch), 64 G TW threads: wave w holds head
 // g G + w % G, tokens t0 .. t0 + 31 with t0 = 32 (blockIdx.x TW + w / G).
 //
-// MASKS (n <= 256 blocks): two passes over the blocks instead of an index
-// list.  Pass 1 keeps only values (a branch-free median-of-three network) and
-// yields T, the row's npast-th best score.  Pass 2 recomputes the same scores
-// (bitwise identical: same instructions on the same data) and marks the blocks
-// with s > T and with s == T in 256-bit masks; the ties that fill the list are
-// the smallest indices, and the masks give the ascending output order for
-// free.  (Keeping pass 1's scores in registers instead halves the occupancy
-// and measured slower.)  !MASKS: each lane
-// keeps a sorted (score, index) list over ascending indices.
-template <int D, int KP, bool MASKS>
+// Two passes over the blocks, no index lists.  Pass 1 keeps only values (a
+// branch-free median-of-three network) and yields T, the row's npast-th best
+// score, and how many scores lie strictly above it.  Pass 2 recomputes the
+// same scores (bitwise identical: same instructions on the same data) and,
+// chunk by chunk in ascending block order, selects the blocks with s > T and
+// the first of those with s == T that complete the list (ties go to the
+// smallest indices), so the output comes out ascending as it is written.
+// (Keeping pass 1's scores in registers instead halves the occupancy and
+// measured slower.)
+template <int D, int KP>
 __global__ __launch_bounds__(64 * kGateMaxWaves) void gate_mfma_kernel(
     const __bf16 *__restrict__ q, const __bf16 *__restrict__ khl, int32_t *__restrict__ idx, int S,
     int Hq, int Hkv, int G, int B, int n, int topk, int TW, int r0, int R) {
@@ -238,171 +223,86 @@ __global__ __launch_bounds__(64 * kGateMaxWaves) void gate_mfma_kernel(
     };
     int32_t *dst = idx + (((size_t)b * Hq + h) * R + (t - r0)) * topk;
 
-    if constexpr (MASKS) {
-        // pass 1: the npast best values of the lane's blocks, then of the row
-        float val[KP];
+    // pass 1: the npast best values of the lane's blocks, then of the row
+    float val[KP];
 #pragma unroll
-        for (int p = 0; p < KP; ++p) val[p] = (p < KP - npast) ? INFINITY : -INFINITY;
-        for (int c = 0; c * 32 < jend; ++c) {
-            stage(c);
-            __syncthreads();
-            if (c * 32 < own) {
-                const f32x16_t sa = scores(c);
+    for (int p = 0; p < KP; ++p) val[p] = (p < KP - npast) ? INFINITY : -INFINITY;
+    for (int c = 0; c * 32 < jend; ++c) {
+        stage(c);
+        __syncthreads();
+        if (c * 32 < own) {
+            const f32x16_t sa = scores(c);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int j = c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                    value_insert<KP>(val, j < own ? sa[i] : -INFINITY);
-                }
+            for (int i = 0; i < 16; ++i) {
+                const int j = c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                value_insert<KP>(val, j < own ? sa[i] : -INFINITY);
             }
         }
-        float pv[KP];
+    }
+    float pv[KP];
 #pragma unroll
-        for (int p = 0; p < KP; ++p) pv[p] = __shfl_xor(val[p], 32, 64);
+    for (int p = 0; p < KP; ++p) pv[p] = __shfl_xor(val[p], 32, 64);
 #pragma unroll
-        for (int p = 0; p < KP; ++p)
-            if (p >= KP - npast) value_insert<KP>(val, pv[p]);
-        const float T = val[KP - 1];
-        __syncthreads();   // every wave is done with the staging buffers of pass 1
+    for (int p = 0; p < KP; ++p)
+        if (p >= KP - npast) value_insert<KP>(val, pv[p]);
+    const float T = val[KP - 1];
+    int ngt = 0;                   // scores strictly above T: all of them are in the list
+#pragma unroll
+    for (int p = 0; p < KP; ++p) ngt += (p >= KP - npast && val[p] > T) ? 1 : 0;
+    int need = npast - ngt;        // ties at T, smallest indices first
+    int r = 0;
+    __syncthreads();               // every wave is done with the staging buffers of pass 1
 
-        // pass 2: blocks above T and blocks equal to T, 16 bits per chunk
-        uint32_t gtm[4] = {0u, 0u, 0u, 0u}, tim[4] = {0u, 0u, 0u, 0u};
+    // pass 2: per chunk, this lane's blocks above T and equal to T as 16-bit
+    // masks; the half-0 lane interleaves them with its partner's (it holds
+    // blocks 8m .. 8m+3 of the chunk, the partner 8m+4 .. 8m+7) and writes
+    for (int c = 0; c * 32 < jend; ++c) {
+        stage(c);
+        __syncthreads();
+        uint32_t gt = 0u, ti = 0u;
+        if (c * 32 < own) {
+            const f32x16_t sa = scores(c);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            if (c * 32 < jend) {
-                stage(c);
-                __syncthreads();
-                if (c * 32 < own) {
-                    const f32x16_t sa = scores(c);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int j = c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                        const uint32_t bit = 1u << (16 * (c & 1) + i);
-                        if (j < own && sa[i] > T) gtm[c >> 1] |= bit;
-                        if (j < own && sa[i] == T) tim[c >> 1] |= bit;
-                    }
-                }
+            for (int i = 0; i < 16; ++i) {
+                const int j = c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                if (j < own && sa[i] > T) gt |= 1u << i;
+                if (j < own && sa[i] == T) ti |= 1u << i;
             }
         }
-        uint32_t pg[4], pt[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            pg[w] = __shfl_xor(gtm[w], 32, 64);
-            pt[w] = __shfl_xor(tim[w], 32, 64);
-        }
-        if (!valid || half) return;
-        // 256-bit masks over the blocks: chunk c is word c; this lane holds the
-        // even nibbles (blocks 8m .. 8m+3), the partner the odd ones
-        uint32_t fg[8], ft[8];
-        int ngt = 0;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int sh = 16 * (c & 1);
-            fg[c] = spread_nibbles(gtm[c >> 1] >> sh) | (spread_nibbles(pg[c >> 1] >> sh) << 4);
-            ft[c] = spread_nibbles(tim[c >> 1] >> sh) | (spread_nibbles(pt[c >> 1] >> sh) << 4);
-            ngt += __builtin_popcount(fg[c]);
-        }
-        int need = npast - ngt;        // ties at T, smallest indices first
-        int r = 0;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            uint32_t w = ft[c], keep = 0u;
+        const uint32_t pg = __shfl_xor(gt, 32, 64), pt = __shfl_xor(ti, 32, 64);
+        if (valid && !half) {
+            const uint32_t fg = spread_nibbles(gt) | (spread_nibbles(pg) << 4);
+            uint32_t w = spread_nibbles(ti) | (spread_nibbles(pt) << 4), keep = 0u;
             while (need > 0 && w) {
                 const uint32_t low = w & (0u - w);
                 keep |= low;
                 w ^= low;
                 --need;
             }
-            uint32_t f = fg[c] | keep;
+            uint32_t f = fg | keep;
             while (f) {
                 if (r < npast) dst[r] = c * 32 + __builtin_ctz(f);   // npast exactly, unless a score is NaN
                 ++r;
                 f &= f - 1;
             }
         }
-        dst[npast] = own;
-        for (int cc = npast + 1; cc < topk; ++cc) dst[cc] = -1;
-        return;
-    } else {
-        float val[KP];
-        int ix[KP];
-#pragma unroll
-        for (int p = 0; p < KP; ++p) {
-            val[p] = (p < KP - npast) ? INFINITY : -INFINITY;
-            ix[p] = INT_MAX;
-        }
-        for (int c = 0; c * 32 < jend; ++c) {
-            stage(c);
-            __syncthreads();
-            if (c * 32 < own) {
-                const f32x16_t sa = scores(c);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int j = c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-                    if (j < own && sa[i] > val[KP - 1]) list_insert<KP>(val, ix, sa[i], j);
-                }
-            }
-        }
-        // merge the partner lane's live entries: higher score first, then smaller
-        // index.  Both lanes merge at once, so the partner's list is copied whole
-        // before either list changes.
-        float pv[KP];
-        int pj[KP];
-#pragma unroll
-        for (int p = 0; p < KP; ++p) {
-            pv[p] = __shfl_xor(val[p], 32, 64);
-            pj[p] = __shfl_xor(ix[p], 32, 64);
-        }
-#pragma unroll
-        for (int p = 0; p < KP; ++p) {
-            float cs = pv[p];
-            int cj = pj[p];
-            if (p >= KP - npast) {
-#pragma unroll
-                for (int o = 0; o < KP; ++o) {
-                    const bool cc = cs > val[o] || (cs == val[o] && cj < ix[o]);
-                    const float tv = val[o];
-                    const int ti = ix[o];
-                    val[o] = cc ? cs : tv;
-                    ix[o] = cc ? cj : ti;
-                    cs = cc ? tv : cs;
-                    cj = cc ? ti : cj;
-                }
-            }
-        }
-        if (!valid || half) return;
-#pragma unroll
-        for (int p = 0; p < KP; ++p) {
-            if (p >= KP - npast) {
-                int r = 0;
-#pragma unroll
-                for (int o = 0; o < KP; ++o) r += (o >= KP - npast && ix[o] < ix[p]) ? 1 : 0;
-                dst[r] = ix[p];
-            }
-        }
-        dst[npast] = own;
-        for (int cc = npast + 1; cc < topk; ++cc) dst[cc] = -1;
     }
+    if (!valid || half) return;
+    dst[npast] = own;
+    for (int cc = npast + 1; cc < topk; ++cc) dst[cc] = -1;
 }
 
 // Token chunks of 32 per workgroup: G TW waves, at most kGateMaxWaves.
 inline int gate_tw(int G) { return G >= kGateMaxWaves ? 1 : (kGateMaxWaves / G >= 2 ? 2 : 1); }
-
-// Block counts up to this use the two-pass mask selection.
-constexpr int kGateMaskBlocks = 256;
 
 template <int D, int KP>
 static hipError_t gate_mfma_impl(const void *q, const __bf16 *khl, int32_t *idx, const Problem &p,
                                  hipStream_t st) {
     const int TW = gate_tw(p.G);
     dim3 grid((p.R + 32 * TW - 1) / (32 * TW), p.Hkv, p.batch);
-    if (p.n <= kGateMaskBlocks)
-        gate_mfma_kernel<D, KP, true><<<grid, 64 * p.G * TW, 0, st>>>(
-            static_cast<const __bf16 *>(q), khl, idx, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk, TW,
-            p.r0, p.R);
-    else
-        gate_mfma_kernel<D, KP, false><<<grid, 64 * p.G * TW, 0, st>>>(
-            static_cast<const __bf16 *>(q), khl, idx, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk, TW,
-            p.r0, p.R);
+    gate_mfma_kernel<D, KP><<<grid, 64 * p.G * TW, 0, st>>>(
+        static_cast<const __bf16 *>(q), khl, idx, p.S, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk, TW,
+        p.r0, p.R);
     return hipGetLastError();
 }
 
