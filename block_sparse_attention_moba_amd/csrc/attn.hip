@@ -29,6 +29,13 @@ namespace moba {
 
 enum Mode { kPast = 0, kOwn = 1, kDense = 2 };
 
+// Thread and workgroup indices straight from the hardware registers.  This
+// file is built without IEEE mode, so the device library's index helpers
+// (built with it) are not inlined here: they would be calls, and their
+// results would not be known to be uniform.
+__device__ inline int tid_x() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ inline unsigned wg_x() { return __builtin_amdgcn_workgroup_id_x(); }
+
 constexpr float kRescaleSlack = 8.f;  // log2 units a row max may exceed the running max
 
 struct AttnArgs {
@@ -44,6 +51,7 @@ struct AttnArgs {
     int M;                 // query rows per tile
     long long L;           // number of lists
     unsigned ntiles;       // tiles of OWN / DENSE launches
+    unsigned nwg;          // workgroups of the launch
     float scale_log2;      // log2(e) / sqrt(D)
     unsigned *defer_count;  // tiles whose logit bound fails, for the tracking pass
     unsigned *defer_list;
@@ -62,15 +70,23 @@ struct Tile {
     int t0, h, tend, npast;
 };
 
+// Load of index data written by an earlier kernel, through the constant
+// address space: a scalar load for a uniform address, even after this
+// kernel's own stores (which never touch these arrays).
+template <typename T>
+__device__ inline T ld_index(const T *p) {
+    return *(const __attribute__((address_space(4))) T *)p;
+}
+
 __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, Tile &tl) {
     if (mode == kPast) {
-        if (tile >= a.tile_off[a.L]) return false;
-        const long long lid = a.tile_list[tile];
+        if (tile >= ld_index(a.tile_off + a.L)) return false;
+        const long long lid = ld_index(a.tile_list + tile);
         const int j = (int)(lid % a.n);
         tl.g = (int)((lid / a.n) % a.Hkv);
         tl.b = (int)(lid / ((long long)a.n * a.Hkv));
-        tl.row_begin = a.list_off[lid] + (uint64_t)(tile - a.tile_off[lid]) * a.M;
-        const uint64_t rend = a.list_off[lid + 1];
+        tl.row_begin = ld_index(a.list_off + lid) + (uint64_t)(tile - ld_index(a.tile_off + lid)) * a.M;
+        const uint64_t rend = ld_index(a.list_off + lid + 1);
         tl.nrows = (int)min((uint64_t)a.M, rend - tl.row_begin);
         tl.key_begin = j * a.B;
         tl.nslice = a.B / 32;
@@ -183,10 +199,13 @@ __device__ inline uint4 pack8(const float *f) {
     return __builtin_bit_cast(uint4, v);
 }
 
-__device__ inline uint2 pack4(float a, float b, float c, float d) {
+// Four floats as bf16, in one 64-bit word (a single 8-byte LDS store: split
+// into two 32-bit stores, the second one loses the LDS alias information and
+// the compiler then waits for every LDS-bound load in flight before it).
+__device__ inline uint64_t pack4(float a, float b, float c, float d) {
     bf16x4_t v;
     v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
-    return __builtin_bit_cast(uint2, v);
+    return __builtin_bit_cast(uint64_t, v);
 }
 
 // End of a pipeline step: this wave's loads other than the newest n have
@@ -205,23 +224,38 @@ __device__ __forceinline__ void ring_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// The workgroup meets once this wave's LDS accesses have completed
+// (lgkmcnt = 0); its vector memory accesses in flight are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63, expcnt 7: no wait; lgkmcnt 0
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // One tile.  FAST: the bounded softmax; a tile whose bound fails is appended
 // to the deferred list and left to the tracking pass.  !FAST: running-max
 // tracking.  PAD (PAST only): the block's slice count is not a multiple of 4,
 // so the loop runs up to 2 padding slices that must be emptied.  sK0..sK3 are
 // the K ring slots, sV0..sV3 the V slots; each is its own LDS array, and the
-// caller passes them in by name.
+// caller passes them in by name; sFlag holds one word per wave.
 template <int D, int MODE, bool FAST, bool PAD, int NW>
 __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile, __bf16 *sK0,
                                                __bf16 *sK1, __bf16 *sK2, __bf16 *sK3, __bf16 *sV0,
-                                               __bf16 *sV1, __bf16 *sV2, __bf16 *sV3) {
-    Tile tl;
-    if (!decode_tile(a, MODE, tile, tl)) return;
+                                               __bf16 *sV1, __bf16 *sV2, __bf16 *sV3, int *sFlag) {
     constexpr int RPW = 256 / NW;       // query rows per wave
     constexpr int NG = RPW / 32;        // 32-row column groups per wave
     static_assert(NG >= 1 && RPW * NW == 256, "wave layout");
+    Tile tl;
+    if (!decode_tile(a, MODE, tile, tl)) return;
 
-    const int tid = threadIdx.x;
+    int tid = tid_x();
+    // An opaque copy, so that in the kernels that loop over tiles the
+    // lane-dependent addresses are recomputed per tile instead of hoisted out
+    // of the tile loop, where they would stay live across the key loop.
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(tid));
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;   // wave: scalar
     const int col = lane & 31, half = lane >> 5;
     const __bf16 *__restrict__ qp = static_cast<const __bf16 *>(a.q);
@@ -341,9 +375,9 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         const float *km = a.kmax2 + ((size_t)tl.b * a.Hkv + tl.g) * a.n;
         if (MODE == kDense) {
             kn2 = 0.f;
-            for (int j = 0; j <= tl.tmax / a.B; ++j) kn2 = fmaxf(kn2, km[j]);
+            for (int j = 0; j <= tl.tmax / a.B; ++j) kn2 = fmaxf(kn2, ld_index(km + j));
         } else {
-            kn2 = km[tl.key_begin / a.B];
+            kn2 = ld_index(km + tl.key_begin / a.B);
         }
     }
     constexpr float kBound2 = 64.f * 64.f;
@@ -352,8 +386,16 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         bool in_bound = true;
 #pragma unroll
         for (int g = 0; g < NG; ++g) in_bound = in_bound && qn2[g] * kn2 <= kBound2;
-        if (__syncthreads_or(!in_bound)) {
-            if (threadIdx.x == 0) a.defer_list[atomicAdd(a.defer_count, 1u)] = tile;
+        // Each wave's flag through LDS; the barrier also makes every wave's part
+        // of the first slices visible.
+        const bool wave_bad = __any(!in_bound);     // over all 64 lanes: outside the branch below
+        if (lane == 0) sFlag[wave] = wave_bad;
+        lds_barrier();
+        int f = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) f |= sFlag[w];
+        if (__builtin_amdgcn_readfirstlane(f) != 0) {
+            if (tid == 0) a.defer_list[atomicAdd(a.defer_count, 1u)] = tile;
             return;
         }
     } else {
@@ -594,7 +636,7 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int ch = (dt * 4 + g4) ^ (col & (CPR - 1));
-                *reinterpret_cast<uint2 *>(stage + col * D + ch * 8 + 4 * half) =
+                *reinterpret_cast<uint64_t *>(stage + col * D + ch * 8 + 4 * half) =
                     pack4(oacc[g][dt][4 * g4] * inv[g], oacc[g][dt][4 * g4 + 1] * inv[g],
                           oacc[g][dt][4 * g4 + 2] * inv[g], oacc[g][dt][4 * g4 + 3] * inv[g]);
             }
@@ -639,13 +681,14 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     __shared__ __attribute__((aligned(16))) __bf16 sV0[kS * (D)];   \
     __shared__ __attribute__((aligned(16))) __bf16 sV1[kS * (D)];   \
     __shared__ __attribute__((aligned(16))) __bf16 sV2[kS * (D)];   \
-    __shared__ __attribute__((aligned(16))) __bf16 sV3[kS * (D)];
+    __shared__ __attribute__((aligned(16))) __bf16 sV3[kS * (D)];   \
+    __shared__ int sFlag[8];
 
 template <int D, int MODE, bool PAD>
 __global__ __launch_bounds__(64 * attn_waves<D>(), 1) void attn_bf16_kernel(AttnArgs a) {
     MOBA_RING_ARRAYS(D)
-    attn_bf16_tile<D, MODE, true, PAD, attn_waves<D>()>(a, xcd_tile(blockIdx.x, gridDim.x), sK0, sK1, sK2, sK3, sV0, sV1,
-                                  sV2, sV3);
+    attn_bf16_tile<D, MODE, true, PAD, attn_waves<D>()>(a, xcd_tile(wg_x(), a.nwg), sK0, sK1, sK2, sK3, sV0, sV1,
+                                  sV2, sV3, sFlag);
 }
 
 // Tracking pass: a persistent grid walks the deferred tiles (normally none).
@@ -653,8 +696,8 @@ template <int D, int MODE, bool PAD>
 __global__ __launch_bounds__(64 * attn_waves<D>(), 1) void attn_bf16_track_kernel(AttnArgs a) {
     MOBA_RING_ARRAYS(D)
     const unsigned n = *a.defer_count;
-    for (unsigned i = blockIdx.x; i < n; i += gridDim.x) {
-        attn_bf16_tile<D, MODE, false, PAD, attn_waves<D>()>(a, a.defer_list[i], sK0, sK1, sK2, sK3, sV0, sV1, sV2, sV3);
+    for (unsigned i = wg_x(); i < n; i += a.nwg) {
+        attn_bf16_tile<D, MODE, false, PAD, attn_waves<D>()>(a, a.defer_list[i], sK0, sK1, sK2, sK3, sV0, sV1, sV2, sV3, sFlag);
         __syncthreads();
     }
 }
@@ -675,9 +718,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     __shared__ float ks[kNF][D + 4];
     __shared__ float vs[kNF][D + 4];
     Tile tl;
-    if (!decode_tile(a, MODE, xcd_tile(blockIdx.x, gridDim.x), tl)) return;
+    if (!decode_tile(a, MODE, xcd_tile(wg_x(), a.nwg), tl)) return;
     constexpr int DH = D / 2;
-    const int r = threadIdx.x >> 1, dh = threadIdx.x & 1;
+    const int r = tid_x() >> 1, dh = tid_x() & 1;
     const float *__restrict__ qp = static_cast<const float *>(a.q);
     const float *__restrict__ kp = static_cast<const float *>(a.k);
     const float *__restrict__ vp = static_cast<const float *>(a.v);
@@ -710,7 +753,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     for (int s = 0; s < nsub; ++s) {
         const int kb = tl.key_begin + s * kNF;
         __syncthreads();
-        for (int e = threadIdx.x; e < kNF * D / 4; e += 256) {
+        for (int e = tid_x(); e < kNF * D / 4; e += 256) {
             const int key = e / (D / 4), c4 = e % (D / 4);
             const size_t off = kvbase + (size_t)(kb + key) * rstride + c4 * 4;
             *reinterpret_cast<float4 *>(&ks[key][c4 * 4]) = *reinterpret_cast<const float4 *>(kp + off);
@@ -780,6 +823,7 @@ static AttnArgs make_args(const AttnBuffers &bf, const Problem &p) {
     a.nslot = part_slots(p);
     a.L = (long long)p.batch * p.Hkv * p.n;
     a.ntiles = 0;
+    a.nwg = 0;
     a.M = tile_rows(p);
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.D));
     return a;
@@ -791,8 +835,10 @@ constexpr unsigned kTrackGrid = 256;
 
 // the bounded pass, then the tracking pass over the tiles it deferred
 template <int D, int MODE, bool PAD>
-static void bf16_pair(const AttnArgs &a, unsigned grid, hipStream_t st) {
+static void bf16_pair(AttnArgs a, unsigned grid, hipStream_t st) {
+    a.nwg = grid;
     attn_bf16_kernel<D, MODE, PAD><<<grid, 64 * attn_waves<D>(), 0, st>>>(a);
+    a.nwg = kTrackGrid;
     attn_bf16_track_kernel<D, MODE, PAD><<<kTrackGrid, 64 * attn_waves<D>(), 0, st>>>(a);
 }
 
@@ -814,6 +860,7 @@ static hipError_t attn_launch(AttnArgs a, const Problem &p, unsigned grid, hipSt
             else bf16_pair<128, MODE, false>(a, grid, st);
         }
     } else {
+        a.nwg = grid;
         if (p.D == 64) attn_f32_kernel<64, MODE><<<grid, 256, 0, st>>>(a);
         else attn_f32_kernel<128, MODE><<<grid, 256, 0, st>>>(a);
     }
