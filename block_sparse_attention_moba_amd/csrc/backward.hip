@@ -24,6 +24,8 @@
 //                     block's list, then the block's own rows, causal) and owns
 //                     dV (first pass) or dK (second pass) of its keys, so no
 //                     atomics and no reduction.
+#include <type_traits>
+
 #include "moba_internal.hpp"
 
 namespace moba {
@@ -374,44 +376,54 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
     uint4 qn = {}, gn = {};
     float ln = INFINITY, dn = 0.f;
     int tn = -1;
-    auto row_of = [&](int ci, int rr, int &t, int &h) -> bool {
-        if (ci < nc1) {
-            const long long e = (long long)ci * kBS + rr;
-            if (e >= nlist) return false;
-            const uint64_t rec = a.lists[lbeg + e];
-            t = (int)row_t(rec);
-            h = g * a.G + (int)row_hh(rec);
-            return true;
-        }
-        const int c2 = ci - nc1;
-        t = k0 + (c2 % cph) * kBS + rr;
-        h = g * a.G + c2 / cph;
-        return t < blk_end;
+    // Rows of chunk ci.  Past-list chunks: the list records, loaded one chunk
+    // ahead of the Q / dO loads that need them.  Own chunks: an odometer over
+    // (32-row chunk, head of the group), advanced once per fetch (chunks are
+    // fetched in order).  Every load reads a valid row (rows past the end are
+    // clamped to the last one) and nothing selects on a loaded value before
+    // the chunk's products, so no load is waited for early.  A row past the
+    // end gets t = -1 and log-sum-exp +inf, hence P = 0.
+    auto rec_of = [&](int ci, int rr) -> uint64_t {
+        const long long e = min((long long)ci * kBS + rr, nlist - 1);
+        return a.lists[lbeg + e];
     };
+    uint64_t rec_s = 0, rec_l = 0;     // records of the next chunk to fetch (staging row, row tid)
+    int own_c = 0, own_h = 0;          // odometer of the next own chunk
     auto fetch = [&](int ci) {
-        if (stager) {
-            int t = 0, h = 0;
-            if (row_of(ci, srr, t, h)) {
-                const size_t o = (((size_t)b * a.S + t) * a.Hq + h) * D + scc * 8;
-                qn = *reinterpret_cast<const uint4 *>(a.q + o);
-                gn = *reinterpret_cast<const uint4 *>(a.dout + o);
-            } else {
-                qn = make_uint4(0, 0, 0, 0);
-                gn = make_uint4(0, 0, 0, 0);
+        int ts, hs, tl, hl;
+        bool okl;
+        if (ci < nc1) {
+            ts = (int)row_t(rec_s);
+            hs = g * a.G + (int)row_hh(rec_s);
+            tl = (int)row_t(rec_l);
+            hl = g * a.G + (int)row_hh(rec_l);
+            okl = (long long)ci * kBS + tid < nlist;
+        } else {
+            const int base = k0 + own_c * kBS;
+            ts = min(base + srr, blk_end - 1);
+            hs = hl = g * a.G + own_h;
+            tl = min(base + tid, blk_end - 1);
+            okl = base + tid < blk_end;
+            if (++own_c == cph) {
+                own_c = 0;
+                ++own_h;
             }
+        }
+        if (stager) {
+            const size_t o = (((size_t)b * a.S + ts) * a.Hq + hs) * D + scc * 8;
+            qn = *reinterpret_cast<const uint4 *>(a.q + o);
+            gn = *reinterpret_cast<const uint4 *>(a.dout + o);
         }
         if (tid < kBS) {
-            int t = 0, h = 0;
-            if (row_of(ci, tid, t, h)) {
-                const size_t rid = ((size_t)b * a.Hq + h) * a.S + t;
-                ln = a.l2[rid];
-                dn = a.delta[rid];
-                tn = ci < nc1 ? 0x7fffffff : t;      // past rows see every key
-            } else {
-                ln = INFINITY;
-                dn = 0.f;
-                tn = -1;
-            }
+            const size_t rid = ((size_t)b * a.Hq + hl) * a.S + tl;
+            ln = a.l2[rid];
+            dn = a.delta[rid];
+            tn = !okl ? -1 : ci < nc1 ? 0x7fffffff : tl;      // past rows see every key
+        }
+        // the records of chunk ci + 1
+        if (nlist > 0) {
+            if (stager) rec_s = rec_of(ci + 1, srr);
+            if (tid < kBS) rec_l = rec_of(ci + 1, tid);
         }
     };
     auto store = [&](int buf) {
@@ -420,7 +432,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
             *reinterpret_cast<uint4 *>(&sG[buf][lds_off<D>(srr, scc)]) = gn;
         }
         if (tid < kBS) {
-            sL[buf][tid] = ln;
+            sL[buf][tid] = tn < 0 ? INFINITY : ln;
             sD[buf][tid] = dn;
             sT[buf][tid] = tn;
         }
@@ -433,9 +445,18 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
         for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
     const f32x16_t zero16 = {};
     if (nc > 0) {
+        if (nlist > 0) {
+            if (stager) rec_s = rec_of(0, srr);
+            if (tid < kBS) rec_l = rec_of(0, tid);
+        }
         fetch(0);
         store(0);
     }
+    // The K (and V) operands have landed before the loop.  Without this wait the
+    // compiler, unsure of them on the path where the loop is skipped, waits for
+    // them inside the loop, and so for the next chunk's loads as well: that
+    // would expose the whole gathered-load latency on every chunk.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int c2 = 0; c2 < nc; c2 += 2)
 #pragma unroll
@@ -454,28 +475,40 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(sg, col, kk, half),
                                                              vf[kk], dp, 0, 0, 0);
         }
-        // register i holds row 8 (i / 4) + 4 half + i % 4
+        // register i holds row 8 (i / 4) + 4 half + i % 4.  Keys past the
+        // block's end (a short block) are not masked: they only reach their own
+        // result columns, which are never stored.  Past-list rows see every key;
+        // own rows are masked causally.
         float w[16];
+        auto form_w = [&](auto causal_c) {
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            const int r0 = 8 * i4 + 4 * half;
-            const float4 l4 = *reinterpret_cast<const float4 *>(&sL[buf][r0]);
-            const int4 t4 = *reinterpret_cast<const int4 *>(&sT[buf][r0]);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const int tv[4] = {t4.x, t4.y, t4.z, t4.w};
-            float dvv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (PASS == kPassDK) {
-                const float4 d4 = *reinterpret_cast<const float4 *>(&sD[buf][r0]);
-                dvv[0] = d4.x; dvv[1] = d4.y; dvv[2] = d4.z; dvv[3] = d4.w;
-            }
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int r0 = 8 * i4 + 4 * half;
+                const float4 l4 = *reinterpret_cast<const float4 *>(&sL[buf][r0]);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                float dvv[4] = {0.f, 0.f, 0.f, 0.f};
+                if (PASS == kPassDK) {
+                    const float4 d4 = *reinterpret_cast<const float4 *>(&sD[buf][r0]);
+                    dvv[0] = d4.x; dvv[1] = d4.y; dvv[2] = d4.z; dvv[3] = d4.w;
+                }
+                int tv[4] = {0, 0, 0, 0};
+                if constexpr (decltype(causal_c)::value) {
+                    const int4 t4 = *reinterpret_cast<const int4 *>(&sT[buf][r0]);
+                    tv[0] = t4.x; tv[1] = t4.y; tv[2] = t4.z; tv[3] = t4.w;
+                }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * i4 + e;
-                float pe = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lv[e]));
-                if (!kvalid || key > tv[e]) pe = 0.f;
-                w[i] = PASS == kPassDV ? pe : pe * (dp[i] - dvv[e]);
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * i4 + e;
+                    float pe = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lv[e]));
+                    if constexpr (decltype(causal_c)::value) {
+                        if (key > tv[e]) pe = 0.f;
+                    }
+                    w[i] = PASS == kPassDV ? pe : pe * (dp[i] - dvv[e]);
+                }
             }
-        }
+        };
+        if (ci >= nc1) form_w(std::true_type());
+        else form_w(std::false_type());
         bf16x8_t wb[2];
         pack16(w, wb);
         // dV^T += dO^T P, or dK^T += Q^T dS, over the chunk's 32 rows
