@@ -180,6 +180,7 @@ __device__ inline int swz_v(int r) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) __bf16 lds_bf16_t;
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -622,21 +623,25 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     // every global store writes whole 16-byte pieces of contiguous rows.
     constexpr int LPR = D / 8;          // lanes per row (8 elements each)
     constexpr int RPP = 64 / LPR;       // rows per store pass
-    __bf16 *const ring[8] = {sK0, sK1, sK2, sK3, sV0, sV1, sV2, sV3};
-    __bf16 *stg[NG];
+    // LDS-typed pointers: chosen by a runtime index from an array, plain
+    // pointers would become generic (flat) accesses, and a flat load waits on
+    // the vector-memory counter, i.e. for the previous row's global store.
+    lds_bf16_t *const ring[8] = {(lds_bf16_t *)sK0, (lds_bf16_t *)sK1, (lds_bf16_t *)sK2, (lds_bf16_t *)sK3,
+                                 (lds_bf16_t *)sV0, (lds_bf16_t *)sV1, (lds_bf16_t *)sV2, (lds_bf16_t *)sV3};
+    lds_bf16_t *stg[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) stg[g] = ring[g * NW + wave];
     const bool to_part = MODE == kPast || (MODE == kOwn && tl.npast > 0);
     long long dst[NG];                  // element offset of the row's destination, -1: padding
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-        __bf16 *stage = stg[g];
+        lds_bf16_t *stage = stg[g];
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int ch = (dt * 4 + g4) ^ (col & (CPR - 1));
-                *reinterpret_cast<uint64_t *>(stage + col * D + ch * 8 + 4 * half) =
+                *reinterpret_cast<__attribute__((address_space(3))) uint64_t *>(stage + col * D + ch * 8 + 4 * half) =
                     pack4(oacc[g][dt][4 * g4] * inv[g], oacc[g][dt][4 * g4 + 1] * inv[g],
                           oacc[g][dt][4 * g4 + 2] * inv[g], oacc[g][dt][4 * g4 + 3] * inv[g]);
             }
@@ -658,14 +663,15 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     __bf16 *base = static_cast<__bf16 *>(to_part ? a.part_o : a.out);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-        const __bf16 *stage = stg[g];
+        const lds_bf16_t *stage = stg[g];
 #pragma unroll
         for (int it = 0; it < 32 / RPP; ++it) {
             const int rr = it * RPP + lane / LPR, ch = lane % LPR;
             const long long o = __shfl(dst[g], rr, 64);       // lane rr holds row rr
             if (o >= 0)
-                *reinterpret_cast<uint4 *>(base + o + ch * 8) =
-                    *reinterpret_cast<const uint4 *>(stage + rr * D + ((ch ^ (rr & (CPR - 1))) << 3));
+                *reinterpret_cast<bf16x8_t *>(base + o + ch * 8) =
+                    *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
+                        stage + rr * D + ((ch ^ (rr & (CPR - 1))) << 3));
         }
     }
 }
