@@ -238,6 +238,28 @@ def test_logit_range_bounded_and_tracking_passes(cfg, scale, dev):
     check_rows(cfg, host_arrays(inp), out, idx, rows)
 
 
+@pytest.mark.parametrize("cfg", [
+    small("hot-rows-block128", hq=4, hkv=2, seqlen=1024, block_size=128, topk=3),
+    small("hot-rows-block512", hq=4, hkv=2, seqlen=2048, block_size=512, topk=3),
+], ids=lambda c: c.name)
+def test_single_hot_rows_defer_their_tiles(cfg, dev):
+    """A few query rows scaled by 256 (exact in bf16), each in a different wave
+    of its tiles: the scaling leaves every row's block ranking unchanged, but
+    only those rows break the logit bound (|q| max|k| about 100 in log2 units
+    against 64), so a tile must be deferred whenever any one of its waves
+    holds such a row -- not only the first wave."""
+    log(f"case {cfg.name}")
+    inp = make_inputs(cfg)
+    q = inp["q"].clone()
+    for t, h in ((cfg.block_size + 40, 1), (3 * cfg.block_size - 1, 2), (cfg.seqlen - 100, 3),
+                 (cfg.seqlen - 1, 0)):
+        q[0, t, h] = q[0, t, h] * 256
+    inp = {"q": q, "k": inp["k"], "v": inp["v"]}
+    out, idx = run_gpu(cfg, inp, dev)
+    rows = oracle.all_rows(cfg.batch, cfg.hq, cfg.seqlen)
+    check_rows(cfg, host_arrays(inp), out, idx, rows)
+
+
 def test_bitwise_deterministic(dev):
     cfg = CONFIGS[1]
     moba = _moba()
