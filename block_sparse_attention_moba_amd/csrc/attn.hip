@@ -78,6 +78,12 @@ __device__ inline T ld_index(const T *p) {
     return *(const __attribute__((address_space(4))) T *)p;
 }
 
+// This workgroup's tile: past-block launches are sized by an upper bound on
+// the tile count, so their XCD shares come from the count itself.
+__device__ inline unsigned first_tile(const AttnArgs &a, int mode) {
+    return mode == kPast ? xcd_tile_counted(wg_x(), ld_index(a.tile_off + a.L)) : xcd_tile(wg_x(), a.nwg);
+}
+
 __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, Tile &tl) {
     if (mode == kPast) {
         if (tile >= ld_index(a.tile_off + a.L)) return false;
@@ -693,7 +699,7 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
 template <int D, int MODE, bool PAD>
 __global__ __launch_bounds__(64 * attn_waves<D>(), 1) void attn_bf16_kernel(AttnArgs a) {
     MOBA_RING_ARRAYS(D)
-    attn_bf16_tile<D, MODE, true, PAD, attn_waves<D>()>(a, xcd_tile(wg_x(), a.nwg), sK0, sK1, sK2, sK3, sV0, sV1,
+    attn_bf16_tile<D, MODE, true, PAD, attn_waves<D>()>(a, first_tile(a, MODE), sK0, sK1, sK2, sK3, sV0, sV1,
                                   sV2, sV3, sFlag);
 }
 
@@ -724,7 +730,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     __shared__ float ks[kNF][D + 4];
     __shared__ float vs[kNF][D + 4];
     Tile tl;
-    if (!decode_tile(a, MODE, xcd_tile(wg_x(), a.nwg), tl)) return;
+    if (!decode_tile(a, MODE, first_tile(a, MODE), tl)) return;
     constexpr int DH = D / 2;
     const int r = tid_x() >> 1, dh = tid_x() & 1;
     const float *__restrict__ qp = static_cast<const float *>(a.q);

@@ -168,7 +168,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) __bf16 sK[2][kBS * D];
     __shared__ __attribute__((aligned(16))) __bf16 sV[2][kBS * D];
     DqTile tl;
-    if (!dq_tile<MODE>(a, xcd_tile(blockIdx.x, gridDim.x), tl)) return;
+    // past-block tiles: the grid bounds the count from above (see xcd_tile_counted)
+    const unsigned tile = MODE == kPastTile ? xcd_tile_counted(blockIdx.x, a.tile_off[a.L])
+                                            : xcd_tile(blockIdx.x, gridDim.x);
+    if (!dq_tile<MODE>(a, tile, tl)) return;
     constexpr int CPR = D / 8;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, half = lane >> 5;

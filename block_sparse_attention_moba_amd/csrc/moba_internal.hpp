@@ -44,6 +44,17 @@ __device__ inline uint32_t xcd_tile(uint32_t bid, uint32_t nb) {
     return (bid & 7u) * (nb >> 3) + (bid >> 3);
 }
 
+// The same for a grid that only bounds the tile count from above (past-block
+// tiles, counted on the device): XCD x takes the x-th eighth of the ntl real
+// tiles, so every XCD gets an equal share however loose the bound.  Workgroups
+// past their XCD's share get ntl: no tile.  Needs gridDim.x >= 8 ceil(ntl / 8).
+__device__ inline uint32_t xcd_tile_counted(uint32_t bid, uint32_t ntl) {
+    const uint32_t c = (ntl + 7u) >> 3, i = bid >> 3;
+    if (i >= c) return ntl;
+    const uint32_t t = (bid & 7u) * c + i;
+    return t < ntl ? t : ntl;
+}
+
 // ---- launchers (each returns the launch status) ----
 struct PoolBuffers {
     float *kbar;           // [batch][Hkv][n][D] block means
