@@ -109,6 +109,9 @@ EDGE = [
     small("short-tail-dense", hq=2, hkv=2, seqlen=960, block_size=256, topk=4),
     small("short-tail-d64-b512", batch=2, hq=2, hkv=2, seqlen=1600, head_dim=64,
           block_size=512, topk=2),
+    # 640 blocks: 20 chunks of 32 block means per gate pass
+    small("640-blocks-gate", hq=4, hkv=1, seqlen=64 * 640, head_dim=128, block_size=64,
+          topk=12, planted=12),
 ]
 
 
