@@ -99,7 +99,7 @@ EDGE = [
           planted=6),
     small("fp32-d64-topk1", hq=2, hkv=2, seqlen=512, head_dim=64, dtype="fp32", block_size=64,
           topk=1),
-    # more than 256 blocks: the gate keeps running top-k lists instead of block masks
+    # more than 256 blocks: 10 chunks of 32 block means per gate pass
     small("320-blocks-list-gate", hq=4, hkv=1, seqlen=64 * 320, head_dim=128, block_size=64,
           topk=12, planted=12),
     # a short last block (seqlen not a multiple of block_size)
@@ -143,7 +143,7 @@ CHUNKED = [
     (EDGE[1], 3 * 192),       # 3-block chunks and a 1-block tail, block 192
     (EDGE[4], 256),           # fp32
     (EDGE[5], 7 * 64),        # top-32 over 64 blocks, ragged tail chunk
-    (EDGE[7], 96 * 64),       # list gate
+    (EDGE[7], 96 * 64),       # 320 blocks
     (EDGE[8], 3 * 128),       # short last block in the tail chunk
 ]
 
