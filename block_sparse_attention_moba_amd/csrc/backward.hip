@@ -323,24 +323,68 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const __bf16 *__restric
 constexpr int kKeysPerWG = 256;   // 8 waves x 32 keys
 enum KvPass { kPassDV = 0, kPassDK = 1 };
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) const char lds_char_t;
+typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8_t;
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const f32x4v_t lds_f32x4_t;
+
+// One chunk slot of the kv staging ring: the chunk's 32 Q rows, its 32 dO rows
+// (both [row][D], 16-byte chunks swizzled as lds_off), then 8 x 64 floats of
+// per-row log-sum-exp and delta.
+template <int D>
+constexpr int kv_slot_elems() { return 2 * kBS * D + 2 * 8 * 64; }
+
+// The last part of a slot, per row r of the chunk: D = 128: wave r / 4 moves
+// rows 4 (r / 4) .. + 3, its 64 floats hold their four log-sum-exps, then
+// their four deltas.  D = 64: wave r / 8 moves the log-sum-exps of rows
+// 8 (r / 8) .. + 7, wave r / 8 + 4 their deltas.  Four consecutive rows
+// r0 .. r0 + 3 (r0 a multiple of 4) are contiguous in both.
+
+// End of a pipeline step: this wave's memory operations other than the newest
+// n have completed and its LDS accesses too, then the workgroup meets (the
+// workgroup fence of __syncthreads would wait for every load in flight).
+template <int n>
+__device__ __forceinline__ void kv_ring_barrier() {
+    static_assert(n < 16, "vmcnt immediate");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(n | 0x70);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // One pass over the query rows that attend a workgroup's 256 keys: the
 // block's list (past rows, every key visible), then the block's own rows
 // t >= k0 of every head of the group (causal).  PASS dV: S, P, dV^T += dO^T P.
 // PASS dK: S, dP, dS, dK^T += Q^T dS.  Two passes instead of one keep each
 // under 256 registers, so two waves share a SIMD (one pass holding both
 // accumulators and both operands needs one SIMD per wave); S is computed twice.
+//
+// The rows arrive in chunks of 32 through a ring of 4 LDS slots, moved
+// straight from global memory into LDS (global_load_lds: no registers, no
+// stores): while chunk c is worked on, chunks c + 1 .. c + 3 are in flight.
+// Every wave issues the same four memory operations per chunk (D = 128: its
+// 4 rows of Q, its 4 rows of dO, their log-sum-exps and deltas; D = 64: 8
+// rows of Q or of dO and their log-sum-exps or deltas; plus the list record of
+// its rows 6 chunks ahead, into a register), so one vector-memory count bounds
+// what is still in flight.  A list record is loaded 3 chunks before the rows
+// it addresses, so it has landed when they are issued.  Rows past the list's
+// end reuse its last record and get weight 0; chunks past the last reuse it.
 // grid: (ceil(B / 256) key groups x n blocks x batch * Hkv, rounded up to a
 // multiple of 8), 512 threads.  Consecutive workgroups -- the key groups of one
 // block's list, which read the same query rows -- run on the same XCD.
 template <int D, int PASS>
 __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsigned nwg) {
-    // two chunk buffers: chunk c + 1 is stored while others still read chunk c
-    __shared__ __attribute__((aligned(16))) __bf16 sQ[2][kBS * D];
-    __shared__ __attribute__((aligned(16))) __bf16 sG[2][kBS * D];
-    __shared__ __attribute__((aligned(16))) float sL[2][kBS];
-    __shared__ __attribute__((aligned(16))) float sD[2][kBS];
-    __shared__ __attribute__((aligned(16))) int sT[2][kBS];
-    constexpr int CPR = D / 8;
+    constexpr int SLOT = kv_slot_elems<D>();
+    __shared__ __attribute__((aligned(16))) __bf16 sR0[SLOT];
+    __shared__ __attribute__((aligned(16))) __bf16 sR1[SLOT];
+    __shared__ __attribute__((aligned(16))) __bf16 sR2[SLOT];
+    __shared__ __attribute__((aligned(16))) __bf16 sR3[SLOT];
+    constexpr int CPR = D / 8;        // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;     // rows per 1 KB load
+    constexpr int NV = D == 128 ? 4 : 3;   // vector-memory operations per chunk and wave
     const unsigned wg = xcd_tile(blockIdx.x, gridDim.x);
     if (wg >= nwg) return;
     const int sub = (int)(wg % nsub);
@@ -369,77 +413,81 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
     const uint64_t lbeg = a.list_off[lid];
     const long long nlist = (long long)(a.list_off[lid + 1] - lbeg);
     const int nc1 = (int)((nlist + kBS - 1) / kBS);
-    const int own_rows = blk_end - k0;
-    const int cph = (own_rows + kBS - 1) / kBS;      // own chunks per head
+    const int own_rows = blk_end - k0;               // a multiple of 64: B and S are
+    const int cph = own_rows / kBS;                   // own chunks per head
     const int nc = nc1 + cph * a.G;
 
-    // staging: thread -> one (row, chunk) piece of the Q and dO rows of a chunk
-    const int srr = tid / CPR, scc = tid % CPR;
-    const bool stager = tid < kBS * CPR;
-    uint4 qn = {}, gn = {};
-    float ln = INFINITY, dn = 0.f;
-    int tn = -1;
-    // Rows of chunk ci.  Past-list chunks: the list records, loaded one chunk
-    // ahead of the Q / dO loads that need them.  Own chunks: an odometer over
-    // (32-row chunk, head of the group), advanced once per fetch (chunks are
-    // fetched in order).  Every load reads a valid row (rows past the end are
-    // clamped to the last one) and nothing selects on a loaded value before
-    // the chunk's products, so no load is waited for early.  A row past the
-    // end gets t = -1 and log-sum-exp +inf, hence P = 0.
-    auto rec_of = [&](int ci, int rr) -> uint64_t {
-        const long long e = min((long long)ci * kBS + rr, nlist - 1);
-        return a.lists[lbeg + e];
-    };
-    uint64_t rec_s = 0, rec_l = 0;     // records of the next chunk to fetch (staging row, row tid)
-    int own_c = 0, own_h = 0;          // odometer of the next own chunk
-    auto fetch = [&](int ci) {
-        int ts, hs, tl, hl;
-        bool okl;
-        if (ci < nc1) {
-            ts = (int)row_t(rec_s);
-            hs = g * a.G + (int)row_hh(rec_s);
-            tl = (int)row_t(rec_l);
-            hl = g * a.G + (int)row_hh(rec_l);
-            okl = (long long)ci * kBS + tid < nlist;
+    // ---- loads.  The chunk row whose 16-byte piece this lane moves, the
+    // piece's place in the row, and the lane's constant part of its addresses.
+    // Row, log-sum-exp and list indices fit in 32 bits: the dq partial
+    // workspace holds nslot x D values for every (batch, head, token) row.
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);     // scalar copy, for the LDS bases
+    const int rq = (D == 128 ? wave : (wave & 3)) * RPI + lane / CPR;
+    const int pc = ((lane % CPR) ^ (rq & (CPR - 1))) << 3;
+    const __bf16 *rowA = (D == 128 || wave < 4 ? a.q : a.dout) + pc;   // Q (D = 64: Q or dO)
+    const __bf16 *rowB = a.dout + pc;                                  // dO (D = 128)
+    const unsigned rqHq = (unsigned)rq * (unsigned)a.Hq;
+    // the row whose log-sum-exp (or delta) this lane moves, within the chunk,
+    // and the lane that holds that row's record: D = 128 rows 4 wave + lane % 4,
+    // D = 64 rows 8 (wave % 4) + lane % 8 (lanes beyond those repeat them)
+    const int ld_row = D == 128 ? 4 * wave + (lane & 3) : 8 * (wave & 3) + (lane & 7);
+    const int ld_src = D == 128 ? 16 * (lane & 3) : 8 * (lane & 7);
+    const float *ld_base = (D == 128 ? (lane & 4) != 0 : wave >= 4) ? a.delta : a.l2;
+    const unsigned bSHq = (unsigned)b * a.S * a.Hq, bHq = (unsigned)b * a.Hq, gG = (unsigned)g * a.G;
+
+    // the list record of row rq of chunk x (clamped into the list; a list with
+    // no rows reads a word of the delta array instead, never used)
+    const uint64_t *recp = nlist > 0 ? a.lists + lbeg : reinterpret_cast<const uint64_t *>(a.delta);
+    const long long rlast = nlist > 0 ? nlist - 1 : 0;
+    auto load_rec = [&](int x) -> uint64_t { return recp[min((long long)x * kBS + rq, rlast)]; };
+    int iss_c = 0, iss_h = 0;         // odometer of the next own chunk to issue
+    // Issue the loads of chunk x into slot dst.
+    auto issue = [&](int x, uint64_t rec, __bf16 *dst) {
+        unsigned R, rid;              // this lane's row (token-major) and its log-sum-exp row
+        if (x < nc1) {
+            const unsigned t = row_t(rec), hq = gG + row_hh(rec);
+            R = bSHq + t * (unsigned)a.Hq + hq;
+            rid = __shfl((bHq + hq) * (unsigned)a.S + t, ld_src, 64);
         } else {
-            const int base = k0 + own_c * kBS;
-            ts = min(base + srr, blk_end - 1);
-            hs = hl = g * a.G + own_h;
-            tl = min(base + tid, blk_end - 1);
-            okl = base + tid < blk_end;
-            if (++own_c == cph) {
-                own_c = 0;
-                ++own_h;
+            int c = cph - 1, h = a.G - 1;     // chunks past the last: the last one again
+            if (x < nc) {
+                c = iss_c;
+                h = iss_h;
+                if (++iss_c == cph) {
+                    iss_c = 0;
+                    ++iss_h;
+                }
             }
+            const unsigned t0 = (unsigned)(k0 + c * kBS), hq = gG + (unsigned)h;
+            R = bSHq + t0 * (unsigned)a.Hq + hq + rqHq;
+            rid = (bHq + hq) * (unsigned)a.S + t0 + (unsigned)ld_row;
         }
-        if (stager) {
-            const size_t o = (((size_t)b * a.S + ts) * a.Hq + hs) * D + scc * 8;
-            qn = *reinterpret_cast<const uint4 *>(a.q + o);
-            gn = *reinterpret_cast<const uint4 *>(a.dout + o);
+        __bf16 *d0 = dst + wave_s * RPI * D;
+        if constexpr (D == 128) {
+            __builtin_amdgcn_global_load_lds(rowA + (size_t)R * D, (lds_void_t *)d0, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(rowB + (size_t)R * D, (lds_void_t *)(d0 + kBS * D), 16, 0, 0);
+        } else {
+            __bf16 *d1 = dst + (wave_s >> 2) * kBS * D + (wave_s & 3) * RPI * D;
+            __builtin_amdgcn_global_load_lds(rowA + (size_t)R * D, (lds_void_t *)d1, 16, 0, 0);
         }
-        if (tid < kBS) {
-            const size_t rid = ((size_t)b * a.Hq + hl) * a.S + tl;
-            ln = a.l2[rid];
-            dn = a.delta[rid];
-            tn = !okl ? -1 : ci < nc1 ? 0x7fffffff : tl;      // past rows see every key
-        }
-        // the records of chunk ci + 1
-        if (nlist > 0) {
-            if (stager) rec_s = rec_of(ci + 1, srr);
-            if (tid < kBS) rec_l = rec_of(ci + 1, tid);
-        }
+        __builtin_amdgcn_global_load_lds(ld_base + rid, (lds_void_t *)(dst + 2 * kBS * D + wave_s * 128),
+                                         4, 0, 0);
     };
-    auto store = [&](int buf) {
-        if (stager) {
-            *reinterpret_cast<uint4 *>(&sQ[buf][lds_off<D>(srr, scc)]) = qn;
-            *reinterpret_cast<uint4 *>(&sG[buf][lds_off<D>(srr, scc)]) = gn;
-        }
-        if (tid < kBS) {
-            sL[buf][tid] = tn < 0 ? INFINITY : ln;
-            sD[buf][tid] = dn;
-            sT[buf][tid] = tn;
-        }
-    };
+
+    // ---- products.  LDS byte offsets of the lane's reads within a slot (the
+    // closed forms of lds_off for these lane patterns: the chunk swizzle is an
+    // XOR on address bits 4..7, so the 16-byte row reads of slice kk are at
+    // RB ^ (kk << 5) and the transposing reads of dimension group x at
+    // TB ^ (x << 6), 8 rows further on at + 16 D (D = 128: group x ^ 2)).
+    const int RB = col * 2 * D + ((half ^ (col & (CPR - 1))) << 4);
+    const int tg = lane >> 4, tj = lane & 15;
+    const int trl = 4 * (tg >> 1) + (tj >> 2);
+    const int TB = trl * 2 * D + (((2 * (tg & 1) + ((tj >> 1) & 1)) ^ (trl & (CPR - 1))) << 4) + 8 * (tj & 1);
+    constexpr int HX = D == 128 ? 2 : 0;
+    // log-sum-exp / delta of rows r0 .. r0 + 3 (r0 = 8 i4 + 4 half)
+    const int LB = D == 128 ? 256 * half : 16 * half;
+    constexpr int LI4 = D == 128 ? 512 : 256, LDL = D == 128 ? 16 : 1024;
+    constexpr int QB = 0, GB = kBS * D * 2, LDB = 2 * kBS * D * 2;   // slot regions, bytes
 
     f32x16_t acc[D / 32];
 #pragma unroll
@@ -447,85 +495,136 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
     const f32x16_t zero16 = {};
-    if (nc > 0) {
-        if (nlist > 0) {
-            if (stager) rec_s = rec_of(0, srr);
-            if (tid < kBS) rec_l = rec_of(0, tid);
-        }
-        fetch(0);
-        store(0);
-    }
-    // The K (and V) operands have landed before the loop.  Without this wait the
-    // compiler, unsure of them on the path where the loop is skipped, waits for
-    // them inside the loop, and so for the next chunk's loads as well: that
-    // would expose the whole gathered-load latency on every chunk.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int c2 = 0; c2 < nc; c2 += 2)
+    int cmp_c = 0;                    // own chunk index within its head, for the next own chunk
+
+    // The products of chunk ci, from slot sl.
+    auto compute = [&](int ci, const __bf16 *sl) {
+        // The lane's offsets, redefined per step by empty asm statements (no
+        // instruction): every read then adds the slot's address as an immediate
+        // offset, instead of each (slot, offset) sum being formed once, outside
+        // the loop, and held in a register of its own.
+        int ro[D / 16], tx[D / 32], lb = LB;
 #pragma unroll
-    for (int buf = 0; buf < 2; ++buf) {
-        const int ci = c2 + buf;
-        if (ci >= nc) break;
-        if (ci + 1 < nc) fetch(ci + 1);
-        const __bf16 *sq = sQ[buf], *sg = sG[buf];
+        for (int kk = 0; kk < D / 16; ++kk) {
+            ro[kk] = RB ^ (kk << 5);
+            asm volatile("" : "+v"(ro[kk]));
+        }
+#pragma unroll
+        for (int x = 0; x < D / 32; ++x) {
+            tx[x] = TB ^ (x << 6);
+            asm volatile("" : "+v"(tx[x]));
+        }
+        asm volatile("" : "+v"(lb));
+        const lds_char_t *base = (lds_char_t *)sl;
+        auto rd16 = [&](int off) { return *reinterpret_cast<const lds_bf16x8_t *>(base + off); };
+        auto rd_tr = [&](int off) {
+            return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4_t *)(base + off));
+        };
         // S = Q K^T (and dP = dO V^T): rows = 32 query rows, columns = this wave's keys
         f32x16_t s = zero16, dp = zero16;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(sq, col, kk, half), kf[kk], s,
-                                                        0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd16(QB + ro[kk]), kf[kk], s, 0, 0, 0);
             if (PASS == kPassDK)
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(sg, col, kk, half),
-                                                             vf[kk], dp, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd16(GB + ro[kk]), vf[kk], dp, 0, 0, 0);
         }
         // register i holds row 8 (i / 4) + 4 half + i % 4.  Keys past the
         // block's end (a short block) are not masked: they only reach their own
-        // result columns, which are never stored.  Past-list rows see every key;
-        // own rows are masked causally.
+        // result columns, which are never stored.  Past-list rows see every key
+        // (rows past the list's end none); own rows are masked causally.
+        // lim: weight 0 where the row index within the chunk is >= lim (past),
+        // or < lim (own: row base + r sees key only if r >= key - base).
         float w[16];
-        auto form_w = [&](auto causal_c) {
+        auto form_w = [&](auto kind_c, int lim) {
+            constexpr int kind = decltype(kind_c)::value;   // 0 all rows, 1 rows < lim, 2 rows >= lim
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 const int r0 = 8 * i4 + 4 * half;
-                const float4 l4 = *reinterpret_cast<const float4 *>(&sL[buf][r0]);
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                const f32x4v_t l4 = *reinterpret_cast<const lds_f32x4_t *>(base + LDB + lb + i4 * LI4);
+                const float lv[4] = {l4[0], l4[1], l4[2], l4[3]};
                 float dvv[4] = {0.f, 0.f, 0.f, 0.f};
                 if (PASS == kPassDK) {
-                    const float4 d4 = *reinterpret_cast<const float4 *>(&sD[buf][r0]);
-                    dvv[0] = d4.x; dvv[1] = d4.y; dvv[2] = d4.z; dvv[3] = d4.w;
-                }
-                int tv[4] = {0, 0, 0, 0};
-                if constexpr (decltype(causal_c)::value) {
-                    const int4 t4 = *reinterpret_cast<const int4 *>(&sT[buf][r0]);
-                    tv[0] = t4.x; tv[1] = t4.y; tv[2] = t4.z; tv[3] = t4.w;
+                    const f32x4v_t d4 = *reinterpret_cast<const lds_f32x4_t *>(base + LDB + LDL + lb + i4 * LI4);
+                    dvv[0] = d4[0]; dvv[1] = d4[1]; dvv[2] = d4[2]; dvv[3] = d4[3];
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 4 * i4 + e;
                     float pe = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lv[e]));
-                    if constexpr (decltype(causal_c)::value) {
-                        if (key > tv[e]) pe = 0.f;
+                    if constexpr (kind == 1) {
+                        if (r0 + e >= lim) pe = 0.f;
+                    } else if constexpr (kind == 2) {
+                        if (r0 + e < lim) pe = 0.f;
                     }
                     w[i] = PASS == kPassDV ? pe : pe * (dp[i] - dvv[e]);
                 }
             }
         };
-        if (ci >= nc1) form_w(std::true_type());
-        else form_w(std::false_type());
+        if (ci >= nc) {
+            form_w(std::integral_constant<int, 1>(), 0);
+        } else if (ci >= nc1) {
+            form_w(std::integral_constant<int, 2>(), key - (k0 + cmp_c * kBS));
+            if (++cmp_c == cph) cmp_c = 0;
+        } else if ((ci + 1) * kBS > nlist) {
+            form_w(std::integral_constant<int, 1>(), (int)(nlist - (long long)ci * kBS));
+        } else {
+            form_w(std::integral_constant<int, 0>(), 0);
+        }
         bf16x8_t wb[2];
         pack16(w, wb);
         // dV^T += dO^T P, or dK^T += Q^T dS, over the chunk's 32 rows
-        const __bf16 *src = PASS == kPassDV ? sg : sq;
+        constexpr int SRC = PASS == kPassDV ? GB : QB;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt)
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(src, h2, dt, lane),
-                                                                  wb[h2], acc[dt], 0, 0, 0);
-        // the other buffer was last read before the previous barrier
-        if (ci + 1 < nc) store(buf ^ 1);
-        __syncthreads();
+            for (int dt = 0; dt < D / 32; ++dt) {
+                const bf16x4_t lo = rd_tr(SRC + h2 * 32 * D + tx[dt]);
+                const bf16x4_t hi = rd_tr(SRC + h2 * 32 * D + 16 * D + tx[dt ^ HX]);
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), wb[h2], acc[dt], 0, 0, 0);
+            }
+    };
+
+    // Prologue: the records of chunks 0 .. 2 (waited for, with the K / V
+    // operands: without this wait the compiler, unsure of them on the path
+    // where the loop is skipped, would wait for them inside the loop, and so
+    // for every load in flight), then chunks 0 .. 2 issued, each after the
+    // record 6 chunks ahead of the one being worked on at that point.
+    uint64_t r3 = load_rec(0), r4 = load_rec(1), r5 = load_rec(2);
+    __builtin_amdgcn_s_waitcnt(0);
+    {
+        uint64_t r6 = load_rec(3);
+        issue(0, r3, sR0);
+        r3 = r4; r4 = r5; r5 = r6;
+        r6 = load_rec(4);
+        issue(1, r3, sR1);
+        r3 = r4; r4 = r5; r5 = r6;
+        r6 = load_rec(5);
+        issue(2, r3, sR2);
+        r3 = r4; r4 = r5; r5 = r6;
     }
+    // Step ci: chunk ci has landed (after it: the loads of chunks ci + 1 and
+    // ci + 2 and two records, 2 NV operations), the workgroup meets (so every
+    // wave is done with chunk ci - 1, whose slot now takes chunk ci + 3),
+    // then chunk ci is worked on.
+    auto step = [&](int ci, const __bf16 *cur, __bf16 *nxt) {
+        kv_ring_barrier<2 * NV>();
+        const uint64_t r6 = load_rec(ci + 6);
+        issue(ci + 3, r3, nxt);
+        r3 = r4; r4 = r5; r5 = r6;
+        compute(ci, cur);
+    };
+    // a multiple of 4 steps (the loop has one exit): steps past the last
+    // chunk work on a reloaded copy of it with every weight 0
+    const int nc4 = (nc + 3) & ~3;
+    for (int c4 = 0; c4 < nc4; c4 += 4) {
+        step(c4, sR0, sR3);
+        step(c4 + 1, sR1, sR0);
+        step(c4 + 2, sR2, sR1);
+        step(c4 + 3, sR3, sR2);
+    }
+    __builtin_amdgcn_s_waitcnt(0);     // the chunks loaded past the last have landed
     if (!kvalid) return;
     // lane (key, half) holds dims dt * 32 + 8 (i / 4) + 4 half + i % 4
     __bf16 *dst = (PASS == kPassDV ? a.dv : a.dk) + ((size_t)b * a.S + key) * rstride +
