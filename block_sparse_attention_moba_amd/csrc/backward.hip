@@ -60,29 +60,80 @@ __device__ inline int lds_off(int r, int chunk) {
     return r * D + ((chunk ^ (r & (D / 8 - 1))) << 3);
 }
 
-// Row operand: lane (row = lane % 32, half) gets chunk 2 kk + half of its row.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) const char lds_char_t;
+typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const f32x4v_t lds_f32x4_t;
+
+// Byte offsets of a lane's reads of a block of 32 LDS rows laid out by lds_off.
+//   ro[kk]: the row operand of slice kk -- lane (row = lane % 32, half) gets
+//     chunk 2 kk + half of its row.
+//   lo[dt], hi[dt]: the transposed operand of the products that sum over the
+//     32 rows -- lane (dim = lane % 32, half) receives rows {16 h2 + 4 half + e,
+//     16 h2 + 8 + 4 half + e} (e = 0..3) of dimension dt * 32 + lane % 32, in
+//     the order the matrix-core result registers hold those rows, by two
+//     ds_read_b64_tr_b16 (within 16 lanes, lane j receives element j mod 4 of
+//     the 8 bytes lane 4 e + j / 4 addresses).  Offsets for h2 = 0; rows 16 on
+//     (h2 = 1) are 32 D bytes further, with the same swizzle.
+// In a loop over a ring of LDS slots, refresh() redefines the offsets in place
+// at each step through empty asm statements (no instruction): every read then adds
+// its slot's address as an immediate offset, instead of each (slot, offset)
+// sum being formed once outside the loop and held in a register of its own.
 template <int D>
-__device__ inline bf16x8_t read_row(const __bf16 *s, int r, int kk, int half) {
-    return *reinterpret_cast<const bf16x8_t *>(s + lds_off<D>(r, 2 * kk + half));
+struct ReadOffsets {
+    int ro[D / 16], lo[D / 32], hi[D / 32];
+    __device__ void init(int lane) {
+        const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) ro[kk] = 2 * lds_off<D>(col, 2 * kk + half);
+        const int g = lane >> 4, j = lane & 15;
+        const int r = 4 * (g >> 1) + (j >> 2);
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            const int d = dt * 32 + 16 * (g & 1) + 4 * (j & 3);
+            lo[dt] = 2 * (lds_off<D>(r, d >> 3) + (d & 7));
+            hi[dt] = 2 * (lds_off<D>(r + 8, d >> 3) + (d & 7));
+        }
+    }
+    __device__ void refresh() {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) asm volatile("" : "+v"(ro[kk]));
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+            asm volatile("" : "+v"(lo[dt]));
+            asm volatile("" : "+v"(hi[dt]));
+        }
+    }
+};
+
+// 16 bytes at byte offset off of an LDS block
+__device__ inline bf16x8_t lds_rd16(const __bf16 *s, int off) {
+    return *reinterpret_cast<const lds_bf16x8_t *>((lds_char_t *)s + off);
 }
 
-// Transposed operand for the products that sum over the 32 staged rows: lane
-// (dim = lane % 32, half) receives rows {16 h2 + 4 half + e, 16 h2 + 8 + 4 half + e}
-// (e = 0..3) of dimension dt * 32 + lane % 32, in the order the matrix-core
-// result registers hold those rows.  Two ds_read_b64_tr_b16: within 16 lanes,
-// lane j receives element j mod 4 of the 8 bytes lane 4 e + j / 4 addresses.
+// the transposed operand (see ReadOffsets) of rows 16 h2 .. 16 h2 + 15
 template <int D>
-__device__ inline bf16x8_t read_tr(const __bf16 *s, int h2, int dt, int lane) {
-    const int g = lane >> 4, j = lane & 15;
-    const int r = 16 * h2 + 4 * (g >> 1) + (j >> 2);
-    const int d = dt * 32 + 16 * (g & 1) + 4 * (j & 3);
-    const __bf16 *lo = s + lds_off<D>(r, d >> 3) + (d & 7);
-    const __bf16 *hi = s + lds_off<D>(r + 8, d >> 3) + (d & 7);
-    const bf16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) bf16x4_t *)(lo));
-    const bf16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) bf16x4_t *)(hi));
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+__device__ inline bf16x8_t lds_rd_tr(const __bf16 *s, const ReadOffsets<D> &o, int h2, int dt) {
+    lds_char_t *b = (lds_char_t *)s + h2 * 32 * D;
+    const bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(b + o.lo[dt]));
+    const bf16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(b + o.hi[dt]));
+    return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// End of a pipeline step: this wave's memory operations other than the newest
+// n have completed and its LDS accesses too, then the workgroup meets (the
+// workgroup fence of __syncthreads would wait for every load in flight).
+template <int n>
+__device__ __forceinline__ void ring_barrier() {
+    static_assert(n < 16, "vmcnt immediate");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(n | 0x70);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ inline void pack16(const float (&x)[16], bf16x8_t (&o)[2]) {
@@ -162,17 +213,26 @@ __device__ inline bool dq_tile(const BwdArgs &a, unsigned tile, DqTile &tl) {
     return true;
 }
 
-// 256 rows, 8 waves of 32; keys in slices of 32 staged through two LDS buffers.
+// 256 rows, 8 waves of 32.  The block's keys come in slices of 32 (K and V)
+// through a ring of 4 LDS slots filled straight from global memory
+// (global_load_lds), like the kv passes: slices s + 1 .. s + 3 are in flight
+// while slice s is worked on.  Every wave issues the same loads per slice
+// (D = 128: 4 rows of K and 4 of V; D = 64: 8 rows of K or of V).
 template <int D, int MODE>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
-    __shared__ __attribute__((aligned(16))) __bf16 sK[2][kBS * D];
-    __shared__ __attribute__((aligned(16))) __bf16 sV[2][kBS * D];
+    constexpr int SLOT = 2 * kBS * D;      // K slice, V slice
+    __shared__ __attribute__((aligned(16))) __bf16 sS0[SLOT];
+    __shared__ __attribute__((aligned(16))) __bf16 sS1[SLOT];
+    __shared__ __attribute__((aligned(16))) __bf16 sS2[SLOT];
+    __shared__ __attribute__((aligned(16))) __bf16 sS3[SLOT];
     DqTile tl;
     // past-block tiles: the grid bounds the count from above (see xcd_tile_counted)
     const unsigned tile = MODE == kPastTile ? xcd_tile_counted(blockIdx.x, a.tile_off[a.L])
                                             : xcd_tile(blockIdx.x, gridDim.x);
     if (!dq_tile<MODE>(a, tile, tl)) return;
-    constexpr int CPR = D / 8;
+    constexpr int CPR = D / 8;             // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;          // rows per 1 KB load
+    constexpr int NV = D == 128 ? 2 : 1;   // loads per slice and wave
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, half = lane >> 5;
 
@@ -207,58 +267,65 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     const float l2r = valid ? a.l2[rowid] : INFINITY;
     const float dr = valid ? a.delta[rowid] : 0.f;
 
-    // staging: thread -> (key row, chunk) of a slice
+    // staging: this lane's 16-byte piece of key row rq of a slice.  Every key
+    // row loaded lies before S: past blocks are whole, and an own tile's last
+    // slice ends at its last row rounded up to 32 (S is a multiple of 64).
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const int rq = (D == 128 ? wave : (wave & 3)) * RPI + lane / CPR;
+    const int pc = ((lane % CPR) ^ (rq & (CPR - 1))) << 3;
     const size_t rstride = (size_t)a.Hkv * D;
-    const __bf16 *kb = a.k + ((size_t)tl.b * a.S + tl.key_begin) * rstride + (size_t)tl.g * D;
-    const __bf16 *vb = a.v + ((size_t)tl.b * a.S + tl.key_begin) * rstride + (size_t)tl.g * D;
-    const int sr = tid / CPR, sc = tid % CPR;
-    const bool stager = tid < kBS * CPR;
-    uint4 kn = {}, vn = {};
-    auto fetch = [&](int hs) {
-        if (stager) {
-            const size_t o = (size_t)(hs * kBS + sr) * rstride + sc * 8;
-            kn = *reinterpret_cast<const uint4 *>(kb + o);
-            vn = *reinterpret_cast<const uint4 *>(vb + o);
-        }
-    };
-    auto store = [&](int buf) {
-        if (stager) {
-            *reinterpret_cast<uint4 *>(&sK[buf][lds_off<D>(sr, sc)]) = kn;
-            *reinterpret_cast<uint4 *>(&sV[buf][lds_off<D>(sr, sc)]) = vn;
+    const size_t kvoff = ((size_t)tl.b * a.S + tl.key_begin + rq) * rstride + (size_t)tl.g * D + pc;
+    const __bf16 *srcA = (D == 128 || wave < 4 ? a.k : a.v) + kvoff;   // K (D = 64: K or V)
+    const __bf16 *srcB = a.v + kvoff;                                   // V (D = 128)
+    // slices past the last are the last again (loaded, never used)
+    auto issue = [&](int hs, __bf16 *dst) {
+        const size_t o = (size_t)min(hs, tl.nslice - 1) * kBS * rstride;
+        if constexpr (D == 128) {
+            __bf16 *d0 = dst + wave_s * RPI * D;
+            __builtin_amdgcn_global_load_lds(srcA + o, (lds_void_t *)d0, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(srcB + o, (lds_void_t *)(d0 + kBS * D), 16, 0, 0);
+        } else {
+            __builtin_amdgcn_global_load_lds(
+                srcA + o, (lds_void_t *)(dst + (wave_s >> 2) * kBS * D + (wave_s & 3) * RPI * D), 16, 0, 0);
         }
     };
 
+    ReadOffsets<D> offs;
+    offs.init(lane);
     f32x16_t dq[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) dq[dt][i] = 0.f;
     const f32x16_t zero16 = {};
-    fetch(0);
-    store(0);
-    __syncthreads();
-    for (int hs = 0; hs < tl.nslice; ++hs) {
-        const int buf = hs & 1;
-        if (hs + 1 < tl.nslice) fetch(hs + 1);
-        const __bf16 *k_s = sK[buf], *v_s = sV[buf];
+
+    // The products of slice hs, from slot sl (K, then V).
+    auto compute = [&](int hs, const __bf16 *sl) {
+        offs.refresh();
+        const ReadOffsets<D> &o = offs;
+        const __bf16 *k_s = sl, *v_s = sl + kBS * D;
         // S^T = K Q^T and dP^T = V dO^T: rows = 32 keys, columns = query rows
         f32x16_t s = zero16, dp = zero16;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(k_s, col, kk, half), qf[kk], s,
-                                                        0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row<D>(v_s, col, kk, half), gf[kk],
-                                                         dp, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_rd16(k_s, o.ro[kk]), qf[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_rd16(v_s, o.ro[kk]), gf[kk], dp, 0, 0, 0);
         }
-        // dS^T = P^T (dP^T - delta), P recomputed from the row's log-sum-exp
+        // dS^T = P^T (dP^T - delta), P recomputed from the row's log-sum-exp;
+        // steps past the last slice weigh nothing
         float ds[16];
-        const int kbase = tl.key_begin + hs * kBS + 4 * half;
+        if (hs >= tl.nslice) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = kbase + 8 * (i >> 2) + (i & 3);
-            float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -l2r));
-            if (MODE != kPastTile && key > tq) p = 0.f;
-            ds[i] = p * (dp[i] - dr);
+            for (int i = 0; i < 16; ++i) ds[i] = 0.f;
+        } else {
+            const int kbase = tl.key_begin + hs * kBS + 4 * half;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = kbase + 8 * (i >> 2) + (i & 3);
+                float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -l2r));
+                if (MODE != kPastTile && key > tq) p = 0.f;
+                ds[i] = p * (dp[i] - dr);
+            }
         }
         bf16x8_t db[2];
         pack16(ds, db);
@@ -267,11 +334,34 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt)
-                dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(k_s, h2, dt, lane),
-                                                                 db[h2], dq[dt], 0, 0, 0);
-        if (hs + 1 < tl.nslice) store(buf ^ 1);
-        __syncthreads();
+                dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_rd_tr<D>(k_s, o, h2, dt), db[h2],
+                                                                 dq[dt], 0, 0, 0);
+    };
+
+    issue(0, sS0);
+    issue(1, sS1);
+    issue(2, sS2);
+    // the query rows and the first slices have landed (without this wait the
+    // compiler, unsure of the row loads on the path that skips the loop,
+    // would wait for them inside it, and so for every slice in flight)
+    __builtin_amdgcn_s_waitcnt(0);
+    // Step hs: slice hs has landed (after it: slices hs + 1, hs + 2, 2 NV
+    // loads), the workgroup meets (every wave is done with slice hs - 1,
+    // whose slot takes slice hs + 3), then slice hs is worked on.
+    auto step = [&](int hs, const __bf16 *cur, __bf16 *nxt) {
+        ring_barrier<2 * NV>();
+        issue(hs + 3, nxt);
+        compute(hs, cur);
+    };
+    // a multiple of 4 steps (the loop has one exit)
+    const int ns4 = (tl.nslice + 3) & ~3;
+    for (int h4 = 0; h4 < ns4; h4 += 4) {
+        step(h4, sS0, sS3);
+        step(h4 + 1, sS1, sS0);
+        step(h4 + 2, sS2, sS1);
+        step(h4 + 3, sS3, sS2);
     }
+    __builtin_amdgcn_s_waitcnt(0);     // the slices loaded past the last have landed
     if (!valid) return;
     // lane (row, half) holds dims dt * 32 + 8 (i / 4) + 4 half + i % 4
     __bf16 *dst = a.part_dq + (rowid * a.nslot + slot) * D;
@@ -323,12 +413,6 @@ __global__ __launch_bounds__(256) void bwd_dq_sum_kernel(const __bf16 *__restric
 constexpr int kKeysPerWG = 256;   // 8 waves x 32 keys
 enum KvPass { kPassDV = 0, kPassDK = 1 };
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) const char lds_char_t;
-typedef __attribute__((address_space(3))) const bf16x8_t lds_bf16x8_t;
-typedef float f32x4v_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) const f32x4v_t lds_f32x4_t;
-
 // One chunk slot of the kv staging ring: the chunk's 32 Q rows, its 32 dO rows
 // (both [row][D], 16-byte chunks swizzled as lds_off), then 8 x 64 floats of
 // per-row log-sum-exp and delta.
@@ -340,20 +424,6 @@ constexpr int kv_slot_elems() { return 2 * kBS * D + 2 * 8 * 64; }
 // their four deltas.  D = 64: wave r / 8 moves the log-sum-exps of rows
 // 8 (r / 8) .. + 7, wave r / 8 + 4 their deltas.  Four consecutive rows
 // r0 .. r0 + 3 (r0 a multiple of 4) are contiguous in both.
-
-// End of a pipeline step: this wave's memory operations other than the newest
-// n have completed and its LDS accesses too, then the workgroup meets (the
-// workgroup fence of __syncthreads would wait for every load in flight).
-template <int n>
-__device__ __forceinline__ void kv_ring_barrier() {
-    static_assert(n < 16, "vmcnt immediate");
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(n | 0x70);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
 
 // One pass over the query rows that attend a workgroup's 256 keys: the
 // block's list (past rows, every key visible), then the block's own rows
@@ -474,20 +544,14 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
                                          4, 0, 0);
     };
 
-    // ---- products.  LDS byte offsets of the lane's reads within a slot (the
-    // closed forms of lds_off for these lane patterns: the chunk swizzle is an
-    // XOR on address bits 4..7, so the 16-byte row reads of slice kk are at
-    // RB ^ (kk << 5) and the transposing reads of dimension group x at
-    // TB ^ (x << 6), 8 rows further on at + 16 D (D = 128: group x ^ 2)).
-    const int RB = col * 2 * D + ((half ^ (col & (CPR - 1))) << 4);
-    const int tg = lane >> 4, tj = lane & 15;
-    const int trl = 4 * (tg >> 1) + (tj >> 2);
-    const int TB = trl * 2 * D + (((2 * (tg & 1) + ((tj >> 1) & 1)) ^ (trl & (CPR - 1))) << 4) + 8 * (tj & 1);
-    constexpr int HX = D == 128 ? 2 : 0;
-    // log-sum-exp / delta of rows r0 .. r0 + 3 (r0 = 8 i4 + 4 half)
-    const int LB = D == 128 ? 256 * half : 16 * half;
+    // ---- products
+    ReadOffsets<D> offs;
+    offs.init(lane);
+    // byte offsets of the log-sum-exps of rows r0 .. r0 + 3 (r0 = 8 i4 + 4 half)
+    // in a slot: LDB + lb + i4 LI4; their deltas LDL further on
+    int lb = D == 128 ? 256 * half : 16 * half;
     constexpr int LI4 = D == 128 ? 512 : 256, LDL = D == 128 ? 16 : 1024;
-    constexpr int QB = 0, GB = kBS * D * 2, LDB = 2 * kBS * D * 2;   // slot regions, bytes
+    constexpr int LDB = 2 * kBS * D * 2;
 
     f32x16_t acc[D / 32];
 #pragma unroll
@@ -499,35 +563,18 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
 
     // The products of chunk ci, from slot sl.
     auto compute = [&](int ci, const __bf16 *sl) {
-        // The lane's offsets, redefined per step by empty asm statements (no
-        // instruction): every read then adds the slot's address as an immediate
-        // offset, instead of each (slot, offset) sum being formed once, outside
-        // the loop, and held in a register of its own.
-        int ro[D / 16], tx[D / 32], lb = LB;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-            ro[kk] = RB ^ (kk << 5);
-            asm volatile("" : "+v"(ro[kk]));
-        }
-#pragma unroll
-        for (int x = 0; x < D / 32; ++x) {
-            tx[x] = TB ^ (x << 6);
-            asm volatile("" : "+v"(tx[x]));
-        }
+        offs.refresh();
+        const ReadOffsets<D> &o = offs;
         asm volatile("" : "+v"(lb));
         const lds_char_t *base = (lds_char_t *)sl;
-        auto rd16 = [&](int off) { return *reinterpret_cast<const lds_bf16x8_t *>(base + off); };
-        auto rd_tr = [&](int off) {
-            return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (__attribute__((address_space(3))) bf16x4_t *)(base + off));
-        };
         // S = Q K^T (and dP = dO V^T): rows = 32 query rows, columns = this wave's keys
         f32x16_t s = zero16, dp = zero16;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd16(QB + ro[kk]), kf[kk], s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_rd16(sl, o.ro[kk]), kf[kk], s, 0, 0, 0);
             if (PASS == kPassDK)
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd16(GB + ro[kk]), vf[kk], dp, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_rd16(sl + kBS * D, o.ro[kk]), vf[kk], dp,
+                                                             0, 0, 0);
         }
         // register i holds row 8 (i / 4) + 4 half + i % 4.  Keys past the
         // block's end (a short block) are not masked: they only reach their own
@@ -574,16 +621,13 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
         bf16x8_t wb[2];
         pack16(w, wb);
         // dV^T += dO^T P, or dK^T += Q^T dS, over the chunk's 32 rows
-        constexpr int SRC = PASS == kPassDV ? GB : QB;
+        const __bf16 *src = PASS == kPassDV ? sl + kBS * D : sl;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-                const bf16x4_t lo = rd_tr(SRC + h2 * 32 * D + tx[dt]);
-                const bf16x4_t hi = rd_tr(SRC + h2 * 32 * D + 16 * D + tx[dt ^ HX]);
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), wb[h2], acc[dt], 0, 0, 0);
-            }
+            for (int dt = 0; dt < D / 32; ++dt)
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_rd_tr<D>(src, o, h2, dt), wb[h2],
+                                                                  acc[dt], 0, 0, 0);
     };
 
     // Prologue: the records of chunks 0 .. 2 (waited for, with the K / V
@@ -609,7 +653,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
     // wave is done with chunk ci - 1, whose slot now takes chunk ci + 3),
     // then chunk ci is worked on.
     auto step = [&](int ci, const __bf16 *cur, __bf16 *nxt) {
-        kv_ring_barrier<2 * NV>();
+        ring_barrier<2 * NV>();
         const uint64_t r6 = load_rec(ci + 6);
         issue(ci + 3, r3, nxt);
         r3 = r4; r4 = r5; r5 = r6;
