@@ -418,14 +418,16 @@ def test_backward_matches_oracle(cfg, dev):
         assert rl2 < 1e-2 and rmax < 3e-2, (name, rl2, rmax)
 
 
-@pytest.mark.timeout(400)
-def test_backward_full_size_128k(dev):
-    """The 128K workload's backward at full size: the sum rules over every key
-    of every KV head (past-block lists and own blocks alike), and every element
-    of one KV head group's dq (rows) and dk, dv (keys) in the last 512 tokens
-    against the oracle run on that group from there on (exact by causality;
-    those rows take dq from 11 past blocks, those keys dk, dv from own rows)."""
-    cfg = CONFIGS[3]
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("which", [3, 4], ids=["128k", "1m"])
+def test_backward_full_size(which, dev):
+    """The 128K and 1M workloads' backward at full size (1M: the size the
+    backward bench times): the sum rules over every key of every KV head
+    (past-block lists and own blocks alike), and every element of one KV head
+    group's dq (rows) and dk, dv (keys) in the last 512 tokens against the
+    oracle run on that group from there on (exact by causality; those rows take
+    dq from 11 past blocks, those keys dk, dv from own rows)."""
+    cfg = CONFIGS[which]
     moba = _moba()
     b, S, hq, hkv, d, B, topk = dims(cfg)
     G = hq // hkv
