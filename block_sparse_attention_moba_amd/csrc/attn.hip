@@ -56,6 +56,7 @@ struct AttnArgs {
     unsigned *defer_count;  // tiles whose logit bound fails, for the tracking pass
     unsigned *defer_list;
     float *lse_out;         // optional natural-log LSE of rows written to the output
+    int fuse_merge;         // OWN (bf16): merge rows with past blocks here, no merge kernel
 };
 
 struct Tile {
@@ -240,6 +241,99 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+}
+
+// Online-softmax merge of an own tile's rows with the partial outputs of
+// their past blocks (write-up "MoBA: Mixture of Block Attention",
+// implementation step five), in the tile's epilogue: the same arithmetic as the
+// merge kernel, on the same bf16 own-block row, read from the LDS staging
+// instead of its partial slot.  With l_j the base-2 log-sum-exp of part j and
+// o_j its normalised output: out = sum_j 2^(l_j - M) o_j / sum_j 2^(l_j - M),
+// M the largest l_j.  Lane (row rr, 16-byte piece ch) as in the store pass;
+// two rows per lane at a time, every slot's loads issued before any is used
+// (slots past the row's count read its last slot again and get weight 0).
+template <int D, int NG>
+__device__ __forceinline__ void merge_rows(const AttnArgs &a, const Tile &tl, lds_bf16_t *(&stg)[NG],
+                                           const long long (&dst)[NG], const long long (&prow)[NG],
+                                           const float (&lse)[NG]) {
+    constexpr int CPR = D / 8, LPR = D / 8, RPP = 64 / LPR;
+    const int lane = tid_x() & 63, ch = lane % LPR;
+    const int np = tl.npast;           // 1 .. kFuseMaxPast
+    const __bf16 *po = static_cast<const __bf16 *>(a.part_o);
+    __bf16 *outp = static_cast<__bf16 *>(a.out);
+    // natural-log LSE index of partial row pr: same (batch, head), token r0 + (pr mod R)
+    const long long lse_shift = ((long long)tl.b * a.Hq + tl.h) * (a.S - a.R) + a.r0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+        for (int it = 0; it < 32 / RPP; it += 2) {
+            int rr[2];
+            long long o[2], pr[2];
+            float lo[2];
+            uint4 pc[2][kFuseMaxPast];
+            float lv[2][kFuseMaxPast];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                rr[u] = (it + u) * RPP + lane / LPR;     // lane rr holds row rr
+                o[u] = __shfl(dst[g], rr[u], 64);
+                pr[u] = __shfl(prow[g], rr[u], 64);
+                lo[u] = __shfl(lse[g], rr[u], 64);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (o[u] < 0) continue;                 // padding row: nothing to merge
+                const __bf16 *src = po + pr[u] * a.nslot * D + ch * 8;
+                const float *ls = a.part_lse + pr[u] * a.nslot;
+#pragma unroll
+                for (int s4 = 0; s4 < kFuseMaxPast; s4 += 4) {
+                    if (s4 >= np) break;
+#pragma unroll
+                    for (int s = s4; s < s4 + 4; ++s) {
+                        const int sc = min(s, np - 1);
+                        pc[u][s] = *reinterpret_cast<const uint4 *>(src + (size_t)sc * D);
+                        lv[u][s] = ls[sc];
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (o[u] < 0) continue;
+                float acc[8];
+                const bf16x8_t own = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
+                    stg[g] + rr[u] * D + ((ch ^ (rr[u] & (CPR - 1))) << 3));
+                unpack8(__builtin_bit_cast(uint4, own), acc);
+                float mx = lo[u];
+#pragma unroll
+                for (int s4 = 0; s4 < kFuseMaxPast; s4 += 4) {
+                    if (s4 >= np) break;
+#pragma unroll
+                    for (int s = s4; s < s4 + 4; ++s) mx = fmaxf(mx, lv[u][s]);
+                }
+                const float w_own = __builtin_amdgcn_exp2f(lo[u] - mx);
+                float wsum = w_own;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] *= w_own;
+#pragma unroll
+                for (int s4 = 0; s4 < kFuseMaxPast; s4 += 4) {
+                    if (s4 >= np) break;
+#pragma unroll
+                    for (int s = s4; s < s4 + 4; ++s) {
+                        const float w = s < np ? __builtin_amdgcn_exp2f(lv[u][s] - mx) : 0.f;
+                        wsum += w;
+                        float f[8];
+                        unpack8(pc[u][s], f);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, f[e], acc[e]);
+                    }
+                }
+                const float iw = 1.f / wsum;
+                if (a.lse_out && ch == 0) a.lse_out[pr[u] + lse_shift] = (mx + __log2f(wsum)) * kLn2;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] *= iw;
+                *reinterpret_cast<uint4 *>(outp + o[u] + ch * 8) = pack8(acc);
+            }
+        }
+    }
 }
 
 // One tile.  FAST: the bounded softmax; a tile whose bound fails is appended
@@ -637,8 +731,12 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     lds_bf16_t *stg[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) stg[g] = ring[g * NW + wave];
-    const bool to_part = MODE == kPast || (MODE == kOwn && tl.npast > 0);
+    // OWN rows with past blocks either go to their partial slot, for the merge
+    // kernel, or (fused) are merged here with the past blocks' partial outputs.
+    const bool fused = MODE == kOwn && tl.npast > 0 && a.fuse_merge;
+    const bool to_part = MODE == kPast || (MODE == kOwn && tl.npast > 0 && !fused);
     long long dst[NG];                  // element offset of the row's destination, -1: padding
+    long long prow[NG];                 // fused: the row's chunk-local partial row
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         lds_bf16_t *stage = stg[g];
@@ -660,12 +758,19 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
                 if (half == 0) a.part_lse[id] = lse[g];
             } else {
                 dst[g] = (((long long)tl.b * a.S + t[g]) * a.Hq + h[g]) * D;
-                if (a.lse_out && half == 0)
+                if (a.lse_out && half == 0 && !fused)
                     a.lse_out[((long long)tl.b * a.Hq + h[g]) * a.S + t[g]] = lse[g] * kLn2;
             }
         }
+        prow[g] = (((long long)tl.b * a.Hq + h[g]) * a.R + (t[g] - a.r0));
     }
     __syncthreads();
+    if constexpr (MODE == kOwn) {
+        if (fused) {
+            merge_rows<D, NG>(a, tl, stg, dst, prow, lse);
+            return;
+        }
+    }
     __bf16 *base = static_cast<__bf16 *>(to_part ? a.part_o : a.out);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -829,6 +934,7 @@ static AttnArgs make_args(const AttnBuffers &bf, const Problem &p) {
     a.defer_count = bf.defer_count;
     a.defer_list = bf.defer_list;
     a.lse_out = bf.lse_out;
+    a.fuse_merge = 0;
     a.batch = p.batch; a.S = p.S; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.B = p.B; a.n = p.n;
     a.r0 = p.r0; a.R = p.R;
     a.topk = p.topk;
@@ -888,6 +994,7 @@ hipError_t launch_attn_past(const AttnBuffers &bf, const Problem &p, uint64_t ti
 hipError_t launch_attn_own(const AttnBuffers &bf, const Problem &p, hipStream_t st) {
     AttnArgs a = make_args(bf, p);
     a.ntiles = (unsigned)own_tiles(p);
+    a.fuse_merge = merge_in_own_pass(p) ? 1 : 0;
     return attn_launch<kOwn>(a, p, round8(a.ntiles), st);
 }
 

@@ -295,7 +295,8 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
             return MOBA_ERR_HIP;
         if ((e = E.mark(MOBA_STAGE_ATTN_OWN)) != hipSuccess) return MOBA_ERR_HIP;
         if ((e = launch_attn_own(bf, p, st)) != hipSuccess) return MOBA_ERR_HIP;
-        if (prow > 0 && (e = launch_merge(bf, p, st)) != hipSuccess) return MOBA_ERR_HIP;
+        if (prow > 0 && !merge_in_own_pass(p) && (e = launch_merge(bf, p, st)) != hipSuccess)
+            return MOBA_ERR_HIP;
     }
     if ((e = E.mark(MOBA_NUM_STAGES)) != hipSuccess) return MOBA_ERR_HIP;
     return MOBA_OK;

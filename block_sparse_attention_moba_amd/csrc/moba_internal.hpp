@@ -121,6 +121,10 @@ inline unsigned long long dense_tiles(const Problem &p) {
 // one for the own block (slot topk - 1), which is written only when the row
 // has past blocks to merge with.
 inline int part_slots(const Problem &p) { return p.topk; }
+// The bf16 own-block pass merges its rows with their past blocks' partial
+// outputs itself (no merge kernel) when a row has at most kFuseMaxPast.
+constexpr int kFuseMaxPast = 12;
+inline bool merge_in_own_pass(const Problem &p) { return p.dtype == kBF16 && p.npast <= kFuseMaxPast; }
 // Backward dq slots per row: past blocks, then the own block (slot - 1).
 inline int bwd_slots(const Problem &p) { return p.topk < p.n ? p.topk : p.n; }
 
