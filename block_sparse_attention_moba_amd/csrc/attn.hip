@@ -263,6 +263,7 @@ __device__ __forceinline__ void merge_rows(const AttnArgs &a, const Tile &tl, ld
     __bf16 *outp = static_cast<__bf16 *>(a.out);
     // natural-log LSE index of partial row pr: same (batch, head), token r0 + (pr mod R)
     const long long lse_shift = ((long long)tl.b * a.Hq + tl.h) * (a.S - a.R) + a.r0;
+    const long long prow_last = (long long)a.batch * a.Hq * a.R - 1;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
 #pragma unroll
@@ -281,7 +282,8 @@ __device__ __forceinline__ void merge_rows(const AttnArgs &a, const Tile &tl, ld
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                if (o[u] < 0) continue;                 // padding row: nothing to merge
+                // a padding row reads some partial row (clamped into the buffer) and stores nothing
+                if (o[u] < 0) pr[u] = min(pr[u], prow_last);
                 const __bf16 *src = po + pr[u] * a.nslot * D + ch * 8;
                 const float *ls = a.part_lse + pr[u] * a.nslot;
 #pragma unroll
@@ -764,13 +766,16 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         }
         prow[g] = (((long long)tl.b * a.Hq + h[g]) * a.R + (t[g] - a.r0));
     }
-    __syncthreads();
+    // Each wave stores only the rows it staged: its own LDS writes precede its
+    // reads in order, so the merge needs no barrier, and its loads of the past
+    // partials start at once.
     if constexpr (MODE == kOwn) {
         if (fused) {
             merge_rows<D, NG>(a, tl, stg, dst, prow, lse);
             return;
         }
     }
+    __syncthreads();
     __bf16 *base = static_cast<__bf16 *>(to_part ? a.part_o : a.out);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
