@@ -766,16 +766,15 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         }
         prow[g] = (((long long)tl.b * a.Hq + h[g]) * a.R + (t[g] - a.r0));
     }
-    // Each wave stores only the rows it staged: its own LDS writes precede its
-    // reads in order, so the merge needs no barrier, and its loads of the past
-    // partials start at once.
+    // Each wave stores (or merges) only the rows it staged: its own LDS writes
+    // precede its reads in order, so no barrier is needed here, and its loads
+    // and stores start at once.
     if constexpr (MODE == kOwn) {
         if (fused) {
             merge_rows<D, NG>(a, tl, stg, dst, prow, lse);
             return;
         }
     }
-    __syncthreads();
     __bf16 *base = static_cast<__bf16 *>(to_part ? a.part_o : a.out);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
