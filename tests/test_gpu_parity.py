@@ -112,6 +112,10 @@ EDGE = [
     # 640 blocks: 20 chunks of 32 block means per gate pass
     small("640-blocks-gate", hq=4, hkv=1, seqlen=64 * 640, head_dim=128, block_size=64,
           topk=12, planted=12),
+    # the merge: in the own-block pass up to 12 past blocks per row (here exactly 12),
+    # the merge kernel beyond (here 13)
+    small("topk13-merge-in-own-pass", hq=4, hkv=2, seqlen=64 * 24, block_size=64, topk=13),
+    small("topk14-merge-kernel", hq=4, hkv=2, seqlen=64 * 24, block_size=64, topk=14),
 ]
 
 
