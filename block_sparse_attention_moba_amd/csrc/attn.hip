@@ -245,11 +245,12 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Online-softmax merge of an own tile's rows with the partial outputs of
 // their past blocks (write-up "MoBA: Mixture of Block Attention",
-// implementation step five), in the tile's epilogue: the same arithmetic as the
-// merge kernel, on the same bf16 own-block row, read from the LDS staging
-// instead of its partial slot.  With l_j the base-2 log-sum-exp of part j and
-// o_j its normalised output: out = sum_j 2^(l_j - M) o_j / sum_j 2^(l_j - M),
-// M the largest l_j.  Lane (row rr, 16-byte piece ch) as in the store pass;
+// implementation step five), in the tile's epilogue: the merge kernel's order
+// of operations (with the hardware exp2 and log2), on the same bf16 own-block
+// row, read from the LDS staging instead of its partial slot.  With l_j the
+// base-2 log-sum-exp of part j and o_j its normalised output:
+// out = sum_j 2^(l_j - M) o_j / sum_j 2^(l_j - M), M the largest l_j.
+// Lane (row rr, 16-byte piece ch) as in the store pass;
 // two rows per lane at a time, every slot's loads issued before any is used
 // (slots past the row's count read its last slot again and get weight 0).
 template <int D, int NG>
@@ -270,7 +271,7 @@ __device__ __forceinline__ void merge_rows(const AttnArgs &a, const Tile &tl, ld
         for (int it = 0; it < 32 / RPP; it += 2) {
             int rr[2];
             long long o[2], pr[2];
-            float lo[2];
+            float lown[2];
             uint4 pc[2][kFuseMaxPast];
             float lv[2][kFuseMaxPast];
 #pragma unroll
@@ -278,7 +279,7 @@ __device__ __forceinline__ void merge_rows(const AttnArgs &a, const Tile &tl, ld
                 rr[u] = (it + u) * RPP + lane / LPR;     // lane rr holds row rr
                 o[u] = __shfl(dst[g], rr[u], 64);
                 pr[u] = __shfl(prow[g], rr[u], 64);
-                lo[u] = __shfl(lse[g], rr[u], 64);
+                lown[u] = __shfl(lse[g], rr[u], 64);
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
@@ -304,14 +305,14 @@ __device__ __forceinline__ void merge_rows(const AttnArgs &a, const Tile &tl, ld
                 const bf16x8_t own = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
                     stg[g] + rr[u] * D + ((ch ^ (rr[u] & (CPR - 1))) << 3));
                 unpack8(__builtin_bit_cast(uint4, own), acc);
-                float mx = lo[u];
+                float mx = lown[u];
 #pragma unroll
                 for (int s4 = 0; s4 < kFuseMaxPast; s4 += 4) {
                     if (s4 >= np) break;
 #pragma unroll
                     for (int s = s4; s < s4 + 4; ++s) mx = fmaxf(mx, lv[u][s]);
                 }
-                const float w_own = __builtin_amdgcn_exp2f(lo[u] - mx);
+                const float w_own = __builtin_amdgcn_exp2f(lown[u] - mx);
                 float wsum = w_own;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[e] *= w_own;
