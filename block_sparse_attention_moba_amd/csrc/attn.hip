@@ -333,7 +333,8 @@ __device__ __forceinline__ void merge_rows(const AttnArgs &a, const Tile &tl, ld
                 if (a.lse_out && ch == 0) a.lse_out[pr[u] + lse_shift] = (mx + __log2f(wsum)) * kLn2;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[e] *= iw;
-                *reinterpret_cast<uint4 *>(outp + o[u] + ch * 8) = pack8(acc);
+                __builtin_nontemporal_store(__builtin_bit_cast(bf16x8_t, pack8(acc)),
+                                            reinterpret_cast<bf16x8_t *>(outp + o[u] + ch * 8));
             }
         }
     }
@@ -758,7 +759,7 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
                 const int sl = MODE == kPast ? slot[g] : a.nslot - 1;
                 const long long id = (((long long)tl.b * a.Hq + h[g]) * a.R + (t[g] - a.r0)) * a.nslot + sl;
                 dst[g] = id * D;
-                if (half == 0) a.part_lse[id] = lse[g];
+                if (half == 0) __builtin_nontemporal_store(lse[g], &a.part_lse[id]);
             } else {
                 dst[g] = (((long long)tl.b * a.S + t[g]) * a.Hq + h[g]) * D;
                 if (a.lse_out && half == 0 && !fused)
@@ -769,7 +770,10 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     }
     // Each wave stores (or merges) only the rows it staged: its own LDS writes
     // precede its reads in order, so no barrier is needed here, and its loads
-    // and stores start at once.
+    // and stores start at once.  Outputs and partial outputs are stored
+    // non-temporally: they are not read again by this launch, and kept out of
+    // L2 they leave it to the K / V slices the XCD's other tiles are streaming
+    // (at 1M, 44 GB fewer re-reads of K / V per launch).
     if constexpr (MODE == kOwn) {
         if (fused) {
             merge_rows<D, NG>(a, tl, stg, dst, prow, lse);
@@ -784,10 +788,11 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         for (int it = 0; it < 32 / RPP; ++it) {
             const int rr = it * RPP + lane / LPR, ch = lane % LPR;
             const long long o = __shfl(dst[g], rr, 64);       // lane rr holds row rr
-            if (o >= 0)
-                *reinterpret_cast<bf16x8_t *>(base + o + ch * 8) =
-                    *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
-                        stage + rr * D + ((ch ^ (rr & (CPR - 1))) << 3));
+            if (o >= 0) {
+                const bf16x8_t v = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t *>(
+                    stage + rr * D + ((ch ^ (rr & (CPR - 1))) << 3));
+                __builtin_nontemporal_store(v, reinterpret_cast<bf16x8_t *>(base + o + ch * 8));
+            }
         }
     }
 }
