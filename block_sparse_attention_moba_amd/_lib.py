@@ -186,7 +186,7 @@ def moba_prefill_varlen(q, k, v, cu_seqlens, block_size, topk, out=None, workspa
         raise ValueError("out must match q in shape and dtype")
     _check(lib().moba_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), arr, ns, hq, hkv, d,
                                      block_size, topk, dt, chunk, _ptr(ws),
-                                     ws.numel() * ws.element_size(), _stream()),
+                                     _nbytes(ws), _stream()),
            "moba_prefill_varlen")
     return out
 
@@ -210,7 +210,7 @@ def moba_prefill_lse(q, k, v, block_size, topk, out=None, lse=None, workspace=No
         raise ValueError("out must match q; lse must be float32 [batch, hq, seqlen]")
     _check(lib().moba_prefill_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), b, S, hq, hkv,
                                   d, block_size, topk, dt, _ptr(ws),
-                                  ws.numel() * ws.element_size(), _stream()), "moba_prefill_lse")
+                                  _nbytes(ws), _stream()), "moba_prefill_lse")
     return out, lse
 
 
@@ -239,15 +239,21 @@ def moba_backward(q, k, v, out, dout, lse, block_size, topk, workspace=None):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     _check(lib().moba_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                                _ptr(dq), _ptr(dk), _ptr(dv), b, S, hq, hkv, d, block_size, topk,
-                               dt, _ptr(ws), ws.numel() * ws.element_size(), _stream()),
+                               dt, _ptr(ws), _nbytes(ws), _stream()),
            "moba_backward")
     return dq, dk, dv
 
 
+def _nbytes(t):
+    """Size of a tensor's storage in bytes (what the C ABI's *_bytes arguments take)."""
+    return t.numel() * t.element_size()
+
+
 def _workspace(nbytes, device, workspace):
     if workspace is not None:
-        if workspace.numel() * workspace.element_size() < nbytes:
-            raise ValueError(f"workspace holds {workspace.numel()} bytes, {nbytes} needed")
+        _need_cuda(workspace)
+        if _nbytes(workspace) < nbytes:
+            raise ValueError(f"workspace holds {_nbytes(workspace)} bytes, {nbytes} needed")
         return workspace
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
@@ -259,9 +265,10 @@ def moba_pool(k, block_size, workspace=None):
     dt = _dtype_code(k)
     _, gb = moba_workspace_size(b, S, hkv, hkv, d, block_size, 1, dt)
     ws = _workspace(gb, k.device, workspace)
-    kbar = torch.empty((b, hkv, S // block_size, d), dtype=torch.float32, device=k.device)
+    n = -(-S // block_size)            # a short last block has its own mean
+    kbar = torch.empty((b, hkv, n, d), dtype=torch.float32, device=k.device)
     _check(lib().moba_pool(_ptr(k), _ptr(kbar), b, S, hkv, d, block_size, dt, _ptr(ws),
-                           ws.numel(), _stream()), "moba_pool")
+                           _nbytes(ws), _stream()), "moba_pool")
     return kbar
 
 
@@ -277,7 +284,7 @@ def moba_gate(q, k, block_size, topk, workspace=None):
     ws = _workspace(gb, q.device, workspace)
     idx = torch.empty((b, hq, S, topk), dtype=torch.int32, device=q.device)
     _check(lib().moba_gate(_ptr(q), _ptr(k), _ptr(idx), b, S, hq, hkv, d, block_size, topk, dt,
-                           _ptr(ws), ws.numel(), _stream()), "moba_gate")
+                           _ptr(ws), _nbytes(ws), _stream()), "moba_gate")
     return idx
 
 
@@ -313,11 +320,11 @@ def moba_prefill(q, k, v, block_size, topk, out=None, workspace=None, stage_even
             raise ValueError("stage_events are not recorded by the chunked prefill")
         _check(lib().moba_prefill_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), b, S, hq, hkv,
                                           d, block_size, topk, dt, query_chunk, _ptr(ws),
-                                          ws.numel() * ws.element_size(), _stream()),
+                                          _nbytes(ws), _stream()),
                "moba_prefill_chunked")
         return out
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), b, S, hq, hkv, d, block_size, topk, dt,
-            _ptr(ws), ws.numel(), _stream())
+            _ptr(ws), _nbytes(ws), _stream())
     if stage_events is None:
         _check(lib().moba_prefill(*args), "moba_prefill")
     else:

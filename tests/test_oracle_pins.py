@@ -205,6 +205,129 @@ def test_mean_selected_blocks_per_row():
     assert mean_sel == pytest.approx(sum(min(b + 1, topk) for b in range(n)) / n)
 
 
+# --------------------------------------------------------------------------- selection check
+
+def _onehot_problem():
+    """Keys of block j are w_j e_j, so K̄_j = w_j e_j and the gate score of block j is q_j w_j.
+
+    Row t=10 (own block 5) scores blocks 0..4 as 0.5, 0.5, 0.375, 0.5, 0.3125;
+    row t=8 (own block 4) scores blocks 0..3 as 3, 1, 6, 2; rows t=2 and t=0
+    sit in blocks 1 and 0.
+    """
+    n, block, d = 6, 2, 6
+    S = n * block
+    w = np.array([1.0, 2.0, 3.0, 1.0, 5.0, 7.0])
+    k = np.zeros((1, S, 1, d), np.float32)
+    for j in range(n):
+        k[0, j * block:(j + 1) * block, 0, j] = w[j]
+    q = np.zeros((1, S, 1, d), np.float32)
+    q[0, 10, 0, :] = [0.5, 0.25, 0.125, 0.5, 0.0625, 9.0]
+    q[0, 8, 0, :] = [3.0, 0.5, 2.0, 2.0, 100.0, 100.0]
+    q[0, 2, 0, :] = [1.0, 1.0, 1.0, 1.0, 1.0, 1.0]
+    kbar = oracle.pool(k, 1, 1, S, 1, d, block)
+    return q, kbar, S, d, block
+
+
+def _gap(q, kbar, S, d, block, topk, ts, sels):
+    rows = np.array([[0, 0, t] for t in ts], np.int64)
+    idx = np.array(sels, np.int32)
+    return oracle.selection_gap(q, 1, kbar, 1, S, 1, 1, d, block, topk, rows, idx)
+
+
+def test_selection_gap_hand_computed_on_one_hot_keys():
+    """Valid selections, correct and wrong, and their gaps (lowest selected minus
+    highest unselected past score) computed by hand from the known scores."""
+    q, kbar, S, d, block = _onehot_problem()
+    cases = [
+        (10, [0, 1, 3, 5], 0.5 - 0.375),      # the oracle's own pick: gap = margin
+        (10, [0, 1, 2, 5], 0.375 - 0.5),      # block 2 (0.375) taken instead of block 3 (0.5)
+        (10, [0, 3, 4, 5], 0.3125 - 0.5),     # block 4 (0.3125) in, blocks 1, 2 out
+        (8, [0, 2, 3, 4], 2.0 - 1.0),         # the oracle's own pick
+        (8, [0, 1, 2, 4], 1.0 - 2.0),         # block 1 (score 1) instead of block 3 (score 2)
+        (8, [1, 2, 3, 4], 1.0 - 3.0),         # block 0 (score 3) left out
+        (2, [0, 1, -1, -1], np.inf),          # every causal block selected: nothing left out
+        (0, [0, -1, -1, -1], np.inf),         # block 0: no past block at all
+    ]
+    valid, gap = _gap(q, kbar, S, d, block, 4, [c[0] for c in cases], [c[1] for c in cases])
+    assert valid.tolist() == [1] * len(cases)
+    np.testing.assert_array_equal(gap, [c[2] for c in cases])
+
+
+def test_selection_gap_rejects_malformed_rows():
+    """Each row breaks exactly one rule of a causal top-k listing and must be invalid."""
+    q, kbar, S, d, block = _onehot_problem()
+    bad = [
+        (10, [1, 0, 3, 5]),       # past blocks not ascending
+        (10, [0, 3, 3, 5]),       # a past block listed twice
+        (10, [0, 1, 3, 4]),       # own block missing (block 4 in its slot)
+        (10, [0, 1, 5, 5]),       # the own block listed as a past block
+        (8, [0, 2, 5, 4]),        # a future block (5 > own block 4) among the past blocks
+        (10, [-1, 0, 1, 5]),      # padding where a past block belongs (too few past blocks)
+        (2, [0, 1, -1, 3]),       # a block in the padding
+        (2, [0, 1, 0, -1]),       # a repeated block in the padding
+        (0, [0, 0, -1, -1]),      # block 0 row with a past entry
+        (2, [1, -1, -1, -1]),     # own block in the past slot, nothing after it
+    ]
+    good = [(10, [0, 1, 3, 5]), (8, [0, 2, 3, 4]), (2, [0, 1, -1, -1]), (0, [0, -1, -1, -1])]
+    rows = bad + good
+    valid, gap = _gap(q, kbar, S, d, block, 4, [r[0] for r in rows], [r[1] for r in rows])
+    assert valid.tolist() == [0] * len(bad) + [1] * len(good)
+
+
+def test_selection_gap_of_oracle_selection_equals_margin():
+    """On planted random inputs (GQA, batch 2, a short last block) the oracle's own
+    selection is valid on every row and its gap is the oracle's margin."""
+    S, hq, hkv, d, block, topk = 200, 4, 2, 8, 16, 4
+    q, k, _ = rand_inputs(S, hq, hkv, d, batch=2, seed=31, planted=3, block=block)
+    rows = oracle.all_rows(2, hq, S)
+    kbar = oracle.pool(k, 1, 2, S, hkv, d, block)
+    idx, margin, _ = oracle.gate(q, 1, kbar, 2, S, hq, hkv, d, block, topk, rows)
+    valid, gap = oracle.selection_gap(q, 1, kbar, 2, S, hq, hkv, d, block, topk, rows, idx)
+    assert np.all(valid == 1)
+    np.testing.assert_allclose(gap, margin, rtol=1e-12, atol=1e-15)
+    assert np.isfinite(margin).sum() > 0
+
+
+def test_selection_gap_of_swapped_selection_matches_numpy_scores():
+    """Swap each row's worst selected past block for its best unselected one; the
+    gap must equal the one computed from numpy block means and numpy dot products."""
+    S, hq, hkv, d, block, topk = 256, 4, 1, 8, 16, 5
+    q, k, _ = rand_inputs(S, hq, hkv, d, seed=33, planted=2, block=block)
+    n = S // block
+    G = hq // hkv
+    kbar_np = k[0].astype(np.float64).reshape(n, block, hkv, d).mean(axis=1)   # [n, hkv, d]
+    rows = oracle.all_rows(1, hq, S)
+    kbar = oracle.pool(k, 1, 1, S, hkv, d, block)
+    idx, margin, _ = oracle.gate(q, 1, kbar, 1, S, hq, hkv, d, block, topk, rows)
+    mut = idx.copy()
+    expect = np.full(len(rows), np.inf)
+    for r, (_, h, t) in enumerate(rows):
+        own = t // block
+        s = kbar_np[:own, h // G] @ q[0, t, h].astype(np.float64)
+        sel = [int(x) for x in idx[r] if 0 <= x < own]
+        rest = [j for j in range(own) if j not in sel]
+        if not sel or not rest:
+            continue
+        worst = min(sel, key=lambda j: s[j])
+        best = max(rest, key=lambda j: s[j])
+        new_sel = sorted([j for j in sel if j != worst] + [best])
+        new_rest = [j for j in range(own) if j not in new_sel]
+        mut[r, :len(new_sel)] = new_sel
+        expect[r] = min(s[new_sel]) - max(s[new_rest])
+    valid, gap = oracle.selection_gap(q, 1, kbar, 1, S, hq, hkv, d, block, topk, rows, mut)
+    assert np.all(valid == 1)
+    swapped = np.isfinite(expect)
+    assert swapped.sum() > 100
+    assert np.all(gap[swapped] < 0)
+    np.testing.assert_allclose(gap, expect, rtol=1e-10, atol=1e-13)
+
+
+def test_selection_gap_rejects_rows_out_of_range():
+    q, kbar, S, d, block = _onehot_problem()
+    with pytest.raises(RuntimeError):
+        _gap(q, kbar, S, d, block, 4, [S], [[0, 1, 2, 3]])
+
+
 # --------------------------------------------------------------------------- attention
 
 @pytest.mark.parametrize("S,hq,hkv,d,block,batch", [
