@@ -411,19 +411,32 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         ld_v[i] = (unsigned)(r * (int)rstride + ((pc ^ swz_v<D>(r)) << 3));
     }
     // slices past the last are clamped to it (loaded again, never used)
-    auto load_k = [&](int hs, __bf16 *dst) {
-        const __bf16 *src = kbase + (size_t)(min(hs, nh - 1) * kS) * rstride;
+    // byte offsets: a uniform base plus a 32-bit lane offset is the load's
+    // scalar-base form, with no 64-bit address arithmetic per load
 #pragma unroll
-        for (int i = 0; i < IPS; ++i)
+    for (int i = 0; i < IPS; ++i) {
+        ld_k[i] *= 2u;
+        ld_v[i] *= 2u;
+    }
+    // (the empty asm keeps the compiler from hoisting the 64-bit lane
+    // addresses out of the key loop, which would cost a 64-bit add per load)
+    auto load_k = [&](int hs, __bf16 *dst) {
+        const char *src = reinterpret_cast<const char *>(kbase + (size_t)(min(hs, nh - 1) * kS) * rstride);
+#pragma unroll
+        for (int i = 0; i < IPS; ++i) {
+            asm volatile("" : "+v"(ld_k[i]));
             __builtin_amdgcn_global_load_lds(src + ld_k[i], (lds_void_t *)(dst + (wave * IPS + i) * 512),
                                              16, 0, 0);
+        }
     };
     auto load_v = [&](int hs, __bf16 *dst) {
-        const __bf16 *src = vbase + (size_t)(min(hs, nh - 1) * kS) * rstride;
+        const char *src = reinterpret_cast<const char *>(vbase + (size_t)(min(hs, nh - 1) * kS) * rstride);
 #pragma unroll
-        for (int i = 0; i < IPS; ++i)
+        for (int i = 0; i < IPS; ++i) {
+            asm volatile("" : "+v"(ld_v[i]));
             __builtin_amdgcn_global_load_lds(src + ld_v[i], (lds_void_t *)(dst + (wave * IPS + i) * 512),
                                              16, 0, 0);
+        }
     };
     // the first slices start moving before Q is even loaded
     load_k(0, sK0);
@@ -450,11 +463,12 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         }
     }
 
-    // Logits in log2 units.  Bounded pass: q <- rne(q * log2(e) / sqrt(d)) in
-    // bf16, so the MFMA yields them directly (the bound keeps |s| <= 64, where
-    // this rounding moves a logit by far less than the bf16 rounding of P).
-    // Tracking pass: raw q, the scale applied in fp32 at the exponent, exact for
-    // logits of any size.  qn2 = |q|^2 in the same units.
+    // Logits in log2 units: the matrix cores take the raw bf16 q (exact), and
+    // the scale log2(e) / sqrt(d) is applied to the fp32 products at the
+    // exponent, in both passes.  (Rounding q * scale to bf16 instead would
+    // move a logit by up to 2^-9 of |q| |k|: with the bound at 64 that is up
+    // to 0.125 log2 units, and keys that tie along different large channels
+    // then get visibly wrong relative weights.)  qn2 = |q|^2 in log2 units.
     const float sl2 = a.scale_log2;
     float qn2[NG];
 #pragma unroll
@@ -463,16 +477,8 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if constexpr (FAST) {
-                    const __bf16 x = (__bf16)((float)qf[g][kk][e] * sl2);
-                    qf[g][kk][e] = x;
-                    acc = fmaf((float)x, (float)x, acc);
-                } else {
-                    acc = fmaf((float)qf[g][kk][e], (float)qf[g][kk][e], acc);
-                }
-            }
-        qn2[g] = (acc + __shfl_xor(acc, 32, 64)) * (FAST ? 1.f : sl2 * sl2);
+            for (int e = 0; e < 8; ++e) acc = fmaf((float)qf[g][kk][e], (float)qf[g][kk][e], acc);
+        qn2[g] = (acc + __shfl_xor(acc, 32, 64)) * (sl2 * sl2);
     }
     // largest squared key norm over the tile's key range
     float kn2;
@@ -595,7 +601,7 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
             }
         }
     };
-    // P = 2^(S - m) (bounded pass: m = 0, S already scaled; tracking pass: the
+    // P = 2^(S c - m) (bounded pass: m = 0, one multiply; tracking pass: the
     // scale folded into the FMA) of column group g, in bf16 for the PV product;
     // the row sums add the same bf16 values, two per dot2.
     const bf16x2_t ones2 = {(__bf16)1.f, (__bf16)1.f};
@@ -604,8 +610,8 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
         for (int i = 0; i < 16; i += 2) {
             float p0, p1;
             if constexpr (decltype(fast_c)::value) {
-                p0 = __builtin_amdgcn_exp2f(sa[g][i]);
-                p1 = __builtin_amdgcn_exp2f(sa[g][i + 1]);
+                p0 = __builtin_amdgcn_exp2f(sa[g][i] * sl2);
+                p1 = __builtin_amdgcn_exp2f(sa[g][i + 1] * sl2);
             } else {
                 p0 = __builtin_amdgcn_exp2f(fmaf(sa[g][i], sl2, -m_run[g]));
                 p1 = __builtin_amdgcn_exp2f(fmaf(sa[g][i + 1], sl2, -m_run[g]));
@@ -689,7 +695,8 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
             VRegs vr;
             read_v(vr, vc);
             ring_barrier<2 * IPS>();
-            read_k(kr, kn + z);
+            if constexpr (MODE == kPast) read_k(kr, kn);
+            else read_k(kr, kn + z);
             load_k(hs + 4, kl);
             load_v(hs + 3, vl);
             pv_group(pb[0], vr, 0);

@@ -22,13 +22,19 @@ TOL = {
 }
 
 
-def selection_report(gpu_idx, ref_idx, margin, valid, gap, dtype):
-    """All inputs are per-row arrays over the same rows.  Returns a dict of counts."""
+def selection_report(gpu_idx, ref_idx, margin, valid, gap, dtype, eps=None):
+    """All inputs are per-row arrays over the same rows.  Returns a dict of counts.
+
+    eps: the near-tie allowance; by default EPS[dtype], sized for gate scores of
+    order one.  The gate's error is relative to |q| |K̄| (bf16 hi + lo parts of
+    the block means, fp32 accumulation), so inputs with much larger scores pass
+    an eps scaled to them.
+    """
     gpu_idx = np.asarray(gpu_idx)
     ref_idx = np.asarray(ref_idx)
     decisive = margin >= DECISIVE
     same = np.all(gpu_idx == ref_idx, axis=1)
-    eps = EPS[dtype]
+    eps = EPS[dtype] if eps is None else eps
     return {
         "rows": int(len(margin)),
         "decisive": int(decisive.sum()),
@@ -38,6 +44,8 @@ def selection_report(gpu_idx, ref_idx, margin, valid, gap, dtype):
         "eps_violations": int((gap < -eps).sum()),
         "exact_all": int(same.sum()),
         "exact_above_eps_mismatch": int(((margin >= eps) & ~same).sum()),
+        "min_gap": float(gap.min()) if len(gap) else float("inf"),
+        "eps": eps,
     }
 
 
