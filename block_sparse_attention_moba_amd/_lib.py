@@ -25,7 +25,10 @@ STAGE_NAMES = ("pool", "gate", "index", "attn_past", "attn_own_merge")
 EXPORTS = ("moba_abi_version", "moba_status_string", "moba_workspace_size", "moba_pool",
            "moba_gate", "moba_prefill", "moba_prefill_timed", "moba_workspace_size_chunked",
            "moba_prefill_chunked", "moba_workspace_size_varlen", "moba_prefill_varlen",
-           "moba_prefill_lse", "moba_workspace_size_backward", "moba_backward")
+           "moba_prefill_lse", "moba_workspace_size_backward", "moba_backward",
+           "moba_prefill_noalloc")
+# bytes of moba_prefill_noalloc's scratch array on each GPU (MOBA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 512 << 20
 
 
 class MobaError(RuntimeError):
@@ -77,6 +80,8 @@ def lib():
     L.moba_workspace_size_backward.argtypes = [ci] * 8 + [ctypes.POINTER(sz)]
     L.moba_backward.restype = ci
     L.moba_backward.argtypes = [vp] * 9 + [ci] * 8 + [vp, sz, vp]
+    L.moba_prefill_noalloc.restype = ci
+    L.moba_prefill_noalloc.argtypes = [vp, vp, vp, vp] + [ci] * 8 + [vp]
     _lib = L
     return L
 
@@ -335,4 +340,26 @@ def moba_prefill(q, k, v, block_size, topk, out=None, workspace=None, stage_even
             e.record()          # make sure the HIP event exists before handing it over
             arr[i] = ctypes.c_void_p(e.cuda_event)
         _check(lib().moba_prefill_timed(*args, arr), "moba_prefill_timed")
+    return out
+
+
+def moba_prefill_noalloc(q, k, v, block_size, topk, out=None):
+    """moba_prefill in the library's own per-GPU scratch array: the call takes no
+    workspace and allocates nothing on the device (``out`` is allocated here
+    only when not given).  Calls that may overlap on one GPU must be serialised."""
+    _need_cuda(q, k, v)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    b, S, hq, d = q.shape
+    hkv = k.shape[2]
+    if k.shape != (b, S, hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [batch, seqlen, num_kv_heads, head_dim]")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda(out)
+    if out.dtype != q.dtype or out.shape != q.shape:
+        raise ValueError("out must match q in shape and dtype")
+    _check(lib().moba_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), b, S, hq, hkv, d,
+                                      block_size, topk, dt, _stream()), "moba_prefill_noalloc")
     return out

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "moba.h"
 #include "moba_internal.hpp"
@@ -216,6 +217,25 @@ moba_status_t varlen_check(const int *cu, int num_seqs, int Hq, int Hkv, int D, 
     return MOBA_OK;
 }
 
+// Pointers of a prefill: present, 16-byte aligned (lse 4-byte), out and lse
+// overlapping no input.
+moba_status_t check_io(const void *q, const void *k, const void *v, const void *out,
+                       const float *lse_out, const Problem &p) {
+    if (!q || !k || !v || !out) return MOBA_ERR_INVALID_ARGUMENT;
+    const size_t qbytes = (size_t)p.batch * p.S * p.Hq * p.D * elem_size(p);
+    const size_t kvbytes = (size_t)p.batch * p.S * p.Hkv * p.D * elem_size(p);
+    if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kvbytes) ||
+        overlaps(out, qbytes, v, kvbytes))
+        return MOBA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(lse_out, 4))
+        return MOBA_ERR_UNSUPPORTED;
+    if (lse_out && (overlaps(lse_out, (size_t)p.batch * p.Hq * p.S * 4, out, qbytes) ||
+                    overlaps(lse_out, (size_t)p.batch * p.Hq * p.S * 4, q, qbytes)))
+        return MOBA_ERR_INVALID_ARGUMENT;
+    return MOBA_OK;
+}
+
 moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *out, int batch,
                            int S, int Hq, int Hkv, int D, int B, int topk, moba_dtype_t dt,
                            int query_chunk, void *ws, size_t ws_bytes, void *stream,
@@ -226,18 +246,8 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
     // query_chunk 0: one pass over the whole sequence (moba_prefill)
     if (query_chunk != 0 && query_chunk % B != 0) return MOBA_ERR_UNSUPPORTED;
     const int C = chunk_len(p, query_chunk);
-    if (!q || !k || !v || !out) return MOBA_ERR_INVALID_ARGUMENT;
-    const size_t qbytes = (size_t)batch * S * Hq * D * elem_size(p);
-    const size_t kvbytes = (size_t)batch * S * Hkv * D * elem_size(p);
-    if (overlaps(out, qbytes, q, qbytes) || overlaps(out, qbytes, k, kvbytes) ||
-        overlaps(out, qbytes, v, kvbytes))
-        return MOBA_ERR_INVALID_ARGUMENT;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
-        !aligned(lse_out, 4))
-        return MOBA_ERR_UNSUPPORTED;
-    if (lse_out && (overlaps(lse_out, (size_t)batch * Hq * S * 4, out, qbytes) ||
-                    overlaps(lse_out, (size_t)batch * Hq * S * 4, q, qbytes)))
-        return MOBA_ERR_INVALID_ARGUMENT;
+    rc = check_io(q, k, v, out, lse_out, p);
+    if (rc != MOBA_OK) return rc;
     const Layout l = prefill_layout(p, C);
     if (ws_bytes < l.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
     if (!ws) return MOBA_ERR_INVALID_ARGUMENT;
@@ -300,6 +310,51 @@ moba_status_t prefill_impl(const void *q, const void *k, const void *v, void *ou
     }
     if ((e = E.mark(MOBA_NUM_STAGES)) != hipSuccess) return MOBA_ERR_HIP;
     return MOBA_OK;
+}
+
+// ---- allocation-free prefill: a fixed scratch array per device ----
+//
+// scratch is this library's own device memory for moba_prefill_noalloc.  Each
+// GPU the library runs on holds its copy until the process ends.  In host code
+// `scratch` only names the array: its device address, different on every
+// device, comes from hipGetSymbolAddress, taken once per device (with that
+// device current) on the first call there and kept in scratch_addr.
+static_assert(MOBA_NOALLOC_SCRATCH_BYTES % kAlign == 0, "scratch size");
+static __device__ __align__(256) char scratch[MOBA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_addr[kMaxDevices];
+
+moba_status_t device_scratch(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOBA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOBA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_addr[dev]) {
+        void *a = nullptr;
+        if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return MOBA_ERR_HIP;
+        if (!aligned(a, kAlign)) return MOBA_ERR_HIP;
+        scratch_addr[dev] = a;
+    }
+    *ptr = scratch_addr[dev];
+    return MOBA_OK;
+}
+
+// Query chunk (tokens, a multiple of B; S for one pass) of the largest
+// chunked prefill whose workspace fits the scratch array, or 0 if not even
+// one block per chunk fits.  The workspace grows with the chunk length.
+int noalloc_chunk(const Problem &p) {
+    const size_t cap = MOBA_NOALLOC_SCRATCH_BYTES;
+    if (p.dense) return prefill_layout(p, p.S).total <= cap ? p.S : 0;
+    if (prefill_layout(p, p.S).total <= cap) return p.S;
+    int lo = 0, hi = p.n;        // blocks per chunk: lo fits (0 = none), hi does not
+    while (hi - lo > 1) {
+        const int mid = lo + (hi - lo) / 2;
+        if (prefill_layout(p, mid * p.B).total <= cap) lo = mid;
+        else hi = mid;
+    }
+    return lo * p.B;
 }
 
 }  // namespace
@@ -400,6 +455,22 @@ moba_status_t moba_prefill_timed(const void *q, const void *k, const void *v, vo
         if (!stage_events[i]) return MOBA_ERR_INVALID_ARGUMENT;
     return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, 0, ws, ws_bytes, stream,
                         stage_events);
+}
+
+moba_status_t moba_prefill_noalloc(const void *q, const void *k, const void *v, void *out,
+                                   int batch, int S, int Hq, int Hkv, int D, int B, int topk,
+                                   moba_dtype_t dt, void *stream) {
+    Problem p;
+    moba_status_t rc = make_problem(batch, S, Hq, Hkv, D, B, topk, dt, &p);
+    if (rc != MOBA_OK) return rc;
+    if ((rc = check_io(q, k, v, out, nullptr, p)) != MOBA_OK) return rc;
+    const int C = noalloc_chunk(p);
+    if (C == 0) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    void *ws = nullptr;
+    const moba_status_t src = device_scratch(&ws);
+    if (src != MOBA_OK) return src;
+    return prefill_impl(q, k, v, out, batch, S, Hq, Hkv, D, B, topk, dt, C >= S ? 0 : C, ws,
+                        MOBA_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 moba_status_t moba_workspace_size_varlen(const int *cu_seqlens, int num_seqs, int Hq, int Hkv,

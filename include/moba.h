@@ -40,7 +40,9 @@
  * Ownership.  Every pointer is caller-owned device memory.  The library
  * allocates nothing, keeps no state between calls and is reentrant: calls on
  * different streams with different workspaces may run concurrently.  Outputs
- * are fully overwritten.  `out` must not overlap q, k or v.
+ * are fully overwritten.  `out` must not overlap q, k or v.  (The one
+ * exception is moba_prefill_noalloc, at the end: it works in a scratch array
+ * of the library's own, shared by its calls on one GPU.)
  *
  * Errors.  The return code is the only channel.  All argument checks run
  * before any HIP call.  Work is asynchronous on `stream` (a hipStream_t; NULL
@@ -244,6 +246,30 @@ moba_status_t moba_backward(const void *q, const void *k, const void *v, const v
                             int batch, int seqlen, int num_q_heads, int num_kv_heads,
                             int head_dim, int block_size, int topk, moba_dtype_t dtype,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Allocation-free moba_prefill, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It takes no workspace: its scratch is a fixed array of
+ * MOBA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; the call itself allocates nothing (no hipMalloc,
+ * no hipFree).  The output is moba_prefill's, bit for bit: the sparse stages
+ * run in query chunks of the most blocks whose scratch fits (one pass when
+ * the whole problem fits).  The GPU is the current device, and `stream` must
+ * belong to it.  Every call on one GPU shares that GPU's scratch array and
+ * leaves its contents behind (each call clears what it reads): calls that may
+ * overlap on one GPU -- on different streams, or from different host
+ * threads -- race and must be serialised by the caller.
+ * Errors as moba_prefill, plus MOBA_ERR_WORKSPACE_TOO_SMALL when even one
+ * block per query chunk needs more scratch than the array holds (at head_dim
+ * 128, 32 query heads and top-k 12 that is a block size above 4096 tokens);
+ * MOBA_ERR_HIP if the array's device address cannot be obtained.
+ */
+#define MOBA_NOALLOC_SCRATCH_BYTES (512ull << 20)
+moba_status_t moba_prefill_noalloc(const void *q, const void *k, const void *v, void *out,
+                                   int batch, int seqlen, int num_q_heads, int num_kv_heads,
+                                   int head_dim, int block_size, int topk, moba_dtype_t dtype,
+                                   void *stream);
 
 #ifdef __cplusplus
 }
