@@ -30,7 +30,13 @@ FLAGS = [
 # quieting of its operands.  Matrix-core results go to ordinary vector
 # registers, so the softmax reads the logits without copies out of the
 # accumulation registers.
-EXTRA = {"attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"attn.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+         # the gate's top-k network compares scores only (NaN inputs give no
+         # defined selection): with NaNs ruled out, min / max / med3 need no
+         # quieting instruction per score.  (IEEE mode stays on: with it off
+         # as well, ROCm 7.2's compiler folds med3(max(-inf, a), b, -inf) to
+         # med3(a, b, a) = a instead of min(a, b), breaking the list.)
+         "gate.hip": ["-fno-honor-nans"]}
 
 
 def hipcc():

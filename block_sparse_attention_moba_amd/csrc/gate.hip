@@ -26,6 +26,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "moba_internal.hpp"
 
 namespace moba {
@@ -292,6 +294,308 @@ __global__ __launch_bounds__(64 * kGateMaxWaves) void gate_mfma_kernel(
     for (int cc = npast + 1; cc < topk; ++cc) dst[cc] = -1;
 }
 
+// ---- bf16, d = 128, n <= 257 blocks: one pass, persistent ----
+//
+// The kernel above computes every score twice (pass 1 finds the threshold,
+// pass 2 recomputes the scores to select against it), and its top-k network
+// is as long as the largest list it supports.  Here every score is computed
+// once and stays in registers (16 per lane and chunk of 32 blocks, at most 8
+// chunks), the value list is exactly npast = topk - 1 long, and rows whose
+// own block is at most topk - 1 (all their past blocks are selected) read no
+// query at all.  Per row:
+//   1. each of the row's two lanes keeps the npast best of its own scores (a
+//      median-of-three insertion network, npast operations per score);
+//   2. the two lists meet through a lane swap: the npast best of the union
+//      are max(A[i], B[npast-1-i]) (A, B sorted descending), so the row's
+//      npast-th best score is T = min_i max(A[i], B[npast-1-i]);
+//   3. the stored scores give the row's blocks with s >= T as bit masks; if
+//      there are exactly npast of them (no tie at T) they are the selection,
+//      otherwise the blocks with s > T plus the smallest-index blocks with
+//      s == T (ties toward the smaller block, as in the rule above).
+// The workgroup is persistent: it walks tiles (one (batch, KV head) pair, 32
+// TW tokens, all G heads) in a static order, heaviest (latest) tiles of each
+// pair first, keeps the pair's block means in LDS while it stays on that
+// pair.  Selected indices are staged per wave in LDS and stored as
+// contiguous rows.
+constexpr int kSpMaxKP = 16;       // npast handled here (topk <= 17)
+
+struct GateSpArgs {
+    const __bf16 *q;
+    const __bf16 *khl;     // [batch][Hkv][n][2][D]
+    int32_t *idx;
+    int S, Hq, Hkv, G, B, n, topk, r0, R;
+    int TW;                // token groups of 32 rows per workgroup (G waves each)
+    int npairs;            // batch * Hkv
+};
+
+// Waves per SIMD: 4 (two 8-wave workgroups per CU, 128 registers) for one
+// chunk, else 2 (256 registers: the scores of up to 8 chunks and the next
+// chunk's accumulators).  The other waves of the SIMD cover a tile's query
+// loads; a next-tile prefetch would cost 32 registers and spill.
+template <int KP, int NCH>
+constexpr int gate_sp_waves() { return NCH == 1 ? 4 : 2; }
+
+template <int KP, int NCH>
+__global__ __launch_bounds__(64 * kGateMaxWaves, (gate_sp_waves<KP, NCH>())) void gate_sp_kernel(
+    GateSpArgs a) {
+    constexpr int D = 128, CPR = D / 8, KD = D / 16;
+    constexpr int TOPK = KP + 1;
+    __shared__ __attribute__((aligned(16))) __bf16 khi[NCH * 32 * D];
+    __shared__ __attribute__((aligned(16))) __bf16 klo[NCH * 32 * D];
+    __shared__ int32_t orow[kGateMaxWaves][32 * TOPK];
+    const int tid = threadIdx.x, nthreads = blockDim.x;
+    const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
+    const int hh = wave % a.G, tg = wave / a.G;
+    int32_t *stage_row = orow[wave];
+    const int nstage = min(a.n, NCH * 32);        // blocks held in LDS
+
+    // per-lane LDS offsets of the A operand (block col of a chunk, 16-byte chunk 2 kk + half)
+    int aoff[KD];
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) aoff[kk] = col * D + (((kk * 2 + half) ^ (col & (CPR - 1))) << 3);
+
+    // Items: (pair, 32-token group), pair-major, the latest (heaviest) token
+    // groups of a pair first.  Workgroup w owns items w, w + grid, w + 2 grid,
+    // ...; its TW token groups (G waves each, one per head) take them in turn
+    // and run independently, so the two waves of a SIMD (different groups)
+    // drift apart and overlap each other's loads, matrix-core and vector work.
+    // They meet only where the pair changes and the block means are restaged.
+    const int n32 = a.R / 32;                          // R is a multiple of 64
+    const long long nitems = (long long)a.npairs * n32;
+    const long long w = blockIdx.x, grid = gridDim.x;
+    auto stage = [&](int pair) {
+        __syncthreads();                               // every wave is done with the last pair
+        const __bf16 *kb = a.khl + (size_t)pair * a.n * 2 * D;
+        for (int it = tid; it < NCH * 32 * CPR; it += nthreads) {
+            const int j = it / CPR, ch = it % CPR;
+            bf16x8_t hi, lo;
+            if (j < nstage) {
+                hi = *reinterpret_cast<const bf16x8_t *>(kb + (size_t)j * 2 * D + ch * 8);
+                lo = *reinterpret_cast<const bf16x8_t *>(kb + (size_t)j * 2 * D + D + ch * 8);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) hi[e] = lo[e] = (__bf16)0.f;
+            }
+            const int off = j * D + ((ch ^ (j & (CPR - 1))) << 3);
+            *reinterpret_cast<bf16x8_t *>(&khi[off]) = hi;
+            *reinterpret_cast<bf16x8_t *>(&klo[off]) = lo;
+        }
+        __syncthreads();
+    };
+    // S^T of chunk c (32 blocks x this wave's 32 rows): lane (col, half) gets
+    // blocks 32 c + 8 (i / 4) + 4 half + i % 4 of row col
+    auto chunk_scores = [&](int c, const bf16x8_t (&qf)[KD]) {
+        f32x16_t acc = {};
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+            const bf16x8_t ah = *reinterpret_cast<const bf16x8_t *>(&khi[c * 32 * D + aoff[kk]]);
+            const bf16x8_t al = *reinterpret_cast<const bf16x8_t *>(&klo[c * 32 * D + aoff[kk]]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[kk], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[kk], acc, 0, 0, 0);
+        }
+        return acc;
+    };
+
+    for (long long k0 = 0;;) {
+        const long long first = w + k0 * grid;
+        if (first >= nitems) break;
+        const int pair = (int)(first / n32);
+        // this workgroup's items of the pair: k0 <= k < k1
+        const long long k1 = ((long long)(pair + 1) * n32 - w + grid - 1) / grid;
+        stage(pair);
+        const int b = pair / a.Hkv, g = pair % a.Hkv, h = g * a.G + hh;
+        for (long long k = k0 + tg; k < k1; k += a.TW) {
+            const int tt32 = n32 - 1 - (int)((w + k * grid) % n32);
+            const int t0 = a.r0 + tt32 * 32;
+            const int own = t0 / a.B;                      // all 32 rows share a block
+            if (own <= a.topk - 1) {
+                // every past block is selected: blocks 0 .. own - 1, the own block, then -1
+                for (int e = lane; e < 32 * a.topk; e += 64) {
+                    const int c = e % a.topk;
+                    stage_row[e] = c < own ? c : (c == own ? own : -1);
+                }
+            } else {
+                bf16x8_t qf[KD];
+                {
+                    const __bf16 *src = a.q + (((size_t)b * a.S + t0 + col) * a.Hq + h) * D + half * 8;
+    #pragma unroll
+                    for (int kk = 0; kk < KD; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t *>(src + kk * 16);
+                }
+                const int nchw = (own + 31) / 32;          // chunks of past blocks (wave-uniform)
+                f32x16_t sc[NCH];
+                float lst[KP];
+    #pragma unroll
+                for (int p = 0; p < KP; ++p) lst[p] = -INFINITY;
+                // the matrix cores compute chunk c + 1 while the vector unit inserts chunk c
+                sc[0] = chunk_scores(0, qf);
+    #pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    if (c + 1 < NCH && c + 1 < nchw) {
+                        sc[c + 1] = chunk_scores(c + 1, qf);
+    #pragma unroll
+                        for (int i = 0; i < 16; ++i) value_insert<KP>(lst, sc[c][i]);
+                    } else if (c + 1 == nchw) {
+                        if (c * 32 + 32 > own) {           // the last chunk holds the own block
+    #pragma unroll
+                            for (int i = 0; i < 16; ++i) {
+                                const int j = c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+                                if (j >= own) sc[c][i] = -INFINITY;
+                            }
+                        }
+    #pragma unroll
+                        for (int i = 0; i < 16; ++i) value_insert<KP>(lst, sc[c][i]);
+                    }
+                }
+                // T: the row's KP-th best score, from this lane's list and its partner's
+                float T = INFINITY;
+    #pragma unroll
+                for (int p = 0; p < KP; ++p) {
+                    const float other = __shfl_xor(lst[KP - 1 - p], 32, 64);
+                    T = fminf(T, fmaxf(lst[p], other));
+                }
+                // the row's blocks with s >= T, one 32-bit mask per chunk (bit j - 32 c)
+                uint32_t m[NCH];
+                int cnt = 0;
+    #pragma unroll
+                for (int c = 0; c < NCH; ++c) {
+                    m[c] = 0u;
+                    if (c < nchw) {
+                        uint32_t b16 = 0u;
+    #pragma unroll
+                        for (int i = 0; i < 16; ++i) b16 |= (sc[c][i] >= T ? 1u : 0u) << i;
+                        cnt += __builtin_popcount(b16);
+                        const uint32_t mine = spread_nibbles(b16) << (4 * half);
+                        m[c] = mine | __shfl_xor(mine, 32, 64);
+                    }
+                }
+                cnt += __shfl_xor(cnt, 32, 64);
+                if (__any(cnt != KP)) {
+                    // ties at T: the blocks above T, then the smallest blocks equal to T
+                    int need = KP;
+                    uint32_t eq[NCH];
+    #pragma unroll
+                    for (int c = 0; c < NCH; ++c) {
+                        eq[c] = 0u;
+                        if (c < nchw) {
+                            uint32_t g16 = 0u, e16 = 0u;
+    #pragma unroll
+                            for (int i = 0; i < 16; ++i) {
+                                g16 |= (sc[c][i] > T ? 1u : 0u) << i;
+                                e16 |= (sc[c][i] == T ? 1u : 0u) << i;
+                            }
+                            const uint32_t gm = spread_nibbles(g16) << (4 * half);
+                            const uint32_t em = spread_nibbles(e16) << (4 * half);
+                            m[c] = gm | __shfl_xor(gm, 32, 64);
+                            eq[c] = em | __shfl_xor(em, 32, 64);
+                            need -= __builtin_popcount(m[c]);
+                        }
+                    }
+    #pragma unroll
+                    for (int c = 0; c < NCH; ++c) {
+                        if (c < nchw) {
+                            uint32_t ew = eq[c];
+                            while (need > 0 && ew) {
+                                const uint32_t low = ew & (0u - ew);
+                                m[c] |= low;
+                                ew ^= low;
+                                --need;
+                            }
+                        }
+                    }
+                }
+                // ascending block indices of the row (half 0 lanes), then the own block
+                if (half == 0) {
+                    int rr = 0;
+    #pragma unroll
+                    for (int c = 0; c < NCH; ++c) {
+                        if (c < nchw) {
+                            uint32_t f = m[c];
+                            while (f) {
+                                if (rr < KP) stage_row[col * TOPK + rr] = c * 32 + __builtin_ctz(f);
+                                ++rr;
+                                f &= f - 1;
+                            }
+                        }
+                    }
+                    for (; rr < KP; ++rr) stage_row[col * TOPK + rr] = -1;   // only with NaN scores
+                    stage_row[col * TOPK + KP] = own;
+                }
+            }
+            // the wave's 32 rows are contiguous in idx: [b][h][t - r0][topk]
+            int32_t *dst = a.idx + (((size_t)b * a.Hq + h) * a.R + (t0 - a.r0)) * a.topk;
+            for (int e = lane; e < 32 * a.topk; e += 64) dst[e] = stage_row[e];
+        }
+        k0 = k1;
+    }
+}
+
+static int device_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
+template <int KP, int NCH>
+static hipError_t gate_sp_launch(const void *q, const __bf16 *khl, int32_t *idx, const Problem &p,
+                                 hipStream_t st) {
+    GateSpArgs a;
+    a.q = static_cast<const __bf16 *>(q);
+    a.khl = khl;
+    a.idx = idx;
+    a.S = p.S; a.Hq = p.Hq; a.Hkv = p.Hkv; a.G = p.G; a.B = p.B; a.n = p.n; a.topk = p.topk;
+    a.TW = p.G >= kGateMaxWaves ? 1 : kGateMaxWaves / p.G;
+    a.r0 = p.r0; a.R = p.R;
+    a.npairs = p.batch * p.Hkv;
+    const long long items = (long long)a.npairs * (p.R / 32);
+    // workgroups per CU: waves per SIMD x 4 SIMDs / waves per workgroup
+    const int wgpc = std::max(1, gate_sp_waves<KP, NCH>() * 4 / (p.G * a.TW));
+    const int grid = (int)std::min<long long>((items + a.TW - 1) / a.TW, (long long)device_cus() * wgpc);
+    if (grid <= 0) return hipSuccess;
+    gate_sp_kernel<KP, NCH><<<grid, 64 * p.G * a.TW, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+template <int KP>
+static hipError_t gate_sp_nch(const void *q, const __bf16 *khl, int32_t *idx, const Problem &p,
+                              hipStream_t st) {
+    const int own_max = (p.r0 + p.R - 1) / p.B;
+    const int nch = (own_max + 31) / 32;
+    if (nch <= 1) return gate_sp_launch<KP, 1>(q, khl, idx, p, st);
+    if (nch <= 2) return gate_sp_launch<KP, 2>(q, khl, idx, p, st);
+    if (nch <= 4) return gate_sp_launch<KP, 4>(q, khl, idx, p, st);
+    return gate_sp_launch<KP, 8>(q, khl, idx, p, st);
+}
+
+static hipError_t gate_sp(const void *q, const __bf16 *khl, int32_t *idx, const Problem &p,
+                          hipStream_t st) {
+    switch (p.npast) {
+    case 1: return gate_sp_nch<1>(q, khl, idx, p, st);
+    case 2: return gate_sp_nch<2>(q, khl, idx, p, st);
+    case 3: return gate_sp_nch<3>(q, khl, idx, p, st);
+    case 4: return gate_sp_nch<4>(q, khl, idx, p, st);
+    case 5: return gate_sp_nch<5>(q, khl, idx, p, st);
+    case 6: return gate_sp_nch<6>(q, khl, idx, p, st);
+    case 7: return gate_sp_nch<7>(q, khl, idx, p, st);
+    case 8: return gate_sp_nch<8>(q, khl, idx, p, st);
+    case 9: return gate_sp_nch<9>(q, khl, idx, p, st);
+    case 10: return gate_sp_nch<10>(q, khl, idx, p, st);
+    case 11: return gate_sp_nch<11>(q, khl, idx, p, st);
+    case 12: return gate_sp_nch<12>(q, khl, idx, p, st);
+    case 13: return gate_sp_nch<13>(q, khl, idx, p, st);
+    case 14: return gate_sp_nch<14>(q, khl, idx, p, st);
+    case 15: return gate_sp_nch<15>(q, khl, idx, p, st);
+    case 16: return gate_sp_nch<16>(q, khl, idx, p, st);
+    default: return hipErrorInvalidValue;       // excluded by launch_gate's dispatch
+    }
+}
+
 // Token chunks of 32 per workgroup: G TW waves, at most kGateMaxWaves.
 inline int gate_tw(int G) { return G >= kGateMaxWaves ? 1 : (kGateMaxWaves / G >= 2 ? 2 : 1); }
 
@@ -359,6 +663,11 @@ hipError_t launch_gate(const void *q, const float *kbar, const __bf16 *khl, int3
         gate_all_kernel<<<grid, 256, 0, st>>>(idx, p.Hq, p.B, p.topk, p.r0, p.R);
         return hipGetLastError();
     }
+    // one pass: bf16, d = 128, topk - 1 == npast <= 16 (not capped by the block count),
+    // past blocks of the chunk's rows in at most 8 chunks of 32
+    if (p.dtype == kBF16 && p.D == 128 && p.G <= kGateMaxWaves && p.npast == p.topk - 1 &&
+        p.npast >= 1 && p.npast <= kSpMaxKP && (p.r0 + p.R - 1) / p.B <= 256)
+        return gate_sp(q, khl, idx, p, st);
     if (p.dtype == kBF16 && p.G <= kGateMaxWaves)
         return p.D == 64 ? gate_mfma_kp<64>(q, khl, idx, p, st) : gate_mfma_kp<128>(q, khl, idx, p, st);
     if (p.dtype == kBF16)

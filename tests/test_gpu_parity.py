@@ -309,6 +309,49 @@ def test_bounded_pass_logits_near_bound_outlier_channels(qa, ka, dev):
     assert orep["rel_l2"] < 5e-3, orep
 
 
+@pytest.mark.parametrize("S,B,topk,tied,strong", [
+    (2048, 128, 4, (3, 5, 7, 9), 1),                 # 16 blocks: one chunk of 32
+    (64 * 80, 64, 4, (3, 33, 40, 65, 70), 1),        # 80 blocks: three chunks
+    (64 * 80, 64, 6, (2, 31, 32, 63, 64, 66), 50),   # ties across chunk edges, top-5 past
+])
+def test_exact_ties_go_to_smaller_blocks(S, B, topk, tied, strong, dev):
+    """Blocks with identical keys have bitwise-equal gate scores on both sides.
+    Every query leans toward them, one stronger block ranks first, so past
+    the last tied block the cut falls inside the tied set: the selection must
+    be the stronger block plus the smallest tied blocks, exactly (the rule
+    breaks ties toward the smaller block; the near-tie allowance would accept
+    either order).  Other rows are checked as usual."""
+    cfg = small(f"ties-{S}-{B}-{topk}", hq=4, hkv=2, seqlen=S, block_size=B, topk=topk)
+    b, _, hq, hkv, d, _, _ = dims(cfg)
+    gen = torch.Generator().manual_seed(S + topk)
+    u = torch.randn((hkv, d), generator=gen)
+    u = u / u.norm(dim=-1, keepdim=True)
+    k = torch.randn((b, S, hkv, d), generator=gen) / d ** 0.5
+    v = torch.randn((b, S, hkv, d), generator=gen) / d ** 0.5
+    q = torch.randn((b, S, hq, d), generator=gen) / d ** 0.5
+    base = k[:, tied[0] * B:(tied[0] + 1) * B].clone() + 2.0 * u
+    for j in tied:
+        k[:, j * B:(j + 1) * B] = base
+    k[:, strong * B:(strong + 1) * B] += 2.5 * u
+    q += 3.0 * u.repeat_interleave(hq // hkv, dim=0)
+    inp = {x: t.to(torch.bfloat16) for x, t in (("q", q), ("k", k), ("v", v))}
+    out, idx = run_gpu(cfg, inp, dev)
+    rows = oracle.all_rows(b, hq, S)
+    arrays = host_arrays(inp)
+    check_rows(cfg, arrays, out, idx, rows, tag=cfg.name)
+    kbar = oracle.pool(arrays[1], arrays[3], b, S, hkv, d, B)
+    ref_idx, _, _ = oracle.gate(arrays[0], arrays[3], kbar, b, S, hq, hkv, d, B, topk, rows)
+    gidx = idx.numpy().reshape(-1, topk)
+    after = rows[:, 2] // B > max(max(tied), strong)
+    expect = sorted([strong] + list(tied))[:topk - 1] if strong < min(tied) else None
+    if expect is None:
+        expect = sorted([strong] + sorted(tied)[:topk - 2])
+    exp_rows = np.array(expect, dtype=np.int32)
+    assert np.array_equal(ref_idx[after][:, :topk - 1], np.tile(exp_rows, (after.sum(), 1)))
+    assert np.array_equal(gidx[after], ref_idx[after]), "tie-break differs from the oracle"
+    log(f"[{cfg.name}] {int(after.sum())} rows with the cut inside the tied blocks: exact")
+
+
 @pytest.mark.parametrize("cfg", [
     small("hot-rows-block128", hq=4, hkv=2, seqlen=1024, block_size=128, topk=3),
     small("hot-rows-block512", hq=4, hkv=2, seqlen=2048, block_size=512, topk=3),
