@@ -168,13 +168,22 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, T
 // goes to the tracking pass, which keeps a running max (moved lazily, only
 // when a row max exceeds it by more than 2^8).
 
-// Waves per workgroup (rows per wave = 256 / NW, in 32-row column groups).
-// d = 128: 8 waves of 32 rows, two per SIMD, so one wave's matrix-core work
-// overlaps the other's vector work (measured: same past-block speed, own-block
-// pass 13% faster than 4 waves of 64 rows).  d = 64: 4 waves of 64 rows (the
+// Rows per tile and waves per workgroup (rows per wave in 32-row column
+// groups).  d = 128: 32 rows per wave, two waves per SIMD, so one wave's
+// matrix-core work overlaps the other's vector work (measured: same
+// past-block speed, own-block pass 13% faster than 4 waves of 64 rows); past-
+// block and dense tiles hold 256 rows (8 waves, one workgroup per CU), own-
+// block tiles 128 (4 waves, two workgroups per CU: one's merge epilogue, bound
+// by HBM, runs beside the other's key loop).  d = 64: 4 waves of 64 rows (the
 // 32-key slice staging needs at least 64 lanes x 16 B per wave).
-template <int D>
-constexpr int attn_waves() { return D == 128 ? 8 : 4; }
+template <int D, int MODE>
+constexpr int attn_rows() { return (D == 128 && MODE == kOwn) ? 128 : 256; }
+template <int D, int MODE>
+constexpr int attn_waves() { return D == 128 ? attn_rows<D, MODE>() / 32 : 4; }
+// waves per SIMD the launch bounds ask for: 2 for the 4-wave d = 128 tiles (two
+// workgroups per CU, at most 256 registers each), else 1
+template <int D, int MODE>
+constexpr int attn_occupancy() { return (D == 128 && attn_waves<D, MODE>() == 4) ? 2 : 1; }
 constexpr int kS = 32;                 // keys per slice
 
 // 16-byte chunk swizzles (XOR on the chunk index within a row)
@@ -350,9 +359,10 @@ template <int D, int MODE, bool FAST, bool PAD, int NW>
 __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile, __bf16 *sK0,
                                                __bf16 *sK1, __bf16 *sK2, __bf16 *sK3, __bf16 *sV0,
                                                __bf16 *sV1, __bf16 *sV2, __bf16 *sV3, int *sFlag) {
-    constexpr int RPW = 256 / NW;       // query rows per wave
+    constexpr int ROWS = attn_rows<D, MODE>();
+    constexpr int RPW = ROWS / NW;      // query rows per wave
     constexpr int NG = RPW / 32;        // 32-row column groups per wave
-    static_assert(NG >= 1 && RPW * NW == 256, "wave layout");
+    static_assert(NG >= 1 && RPW * NW == ROWS, "wave layout");
     Tile tl;
     if (!decode_tile(a, MODE, tile, tl)) return;
 
@@ -819,19 +829,22 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     __shared__ int sFlag[8];
 
 template <int D, int MODE, bool PAD>
-__global__ __launch_bounds__(64 * attn_waves<D>(), 1) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__((64 * attn_waves<D, MODE>()), (attn_occupancy<D, MODE>())) void attn_bf16_kernel(
+    AttnArgs a) {
     MOBA_RING_ARRAYS(D)
-    attn_bf16_tile<D, MODE, true, PAD, attn_waves<D>()>(a, first_tile(a, MODE), sK0, sK1, sK2, sK3, sV0, sV1,
-                                  sV2, sV3, sFlag);
+    attn_bf16_tile<D, MODE, true, PAD, attn_waves<D, MODE>()>(a, first_tile(a, MODE), sK0, sK1, sK2, sK3, sV0,
+                                                             sV1, sV2, sV3, sFlag);
 }
 
 // Tracking pass: a persistent grid walks the deferred tiles (normally none).
 template <int D, int MODE, bool PAD>
-__global__ __launch_bounds__(64 * attn_waves<D>(), 1) void attn_bf16_track_kernel(AttnArgs a) {
+__global__ __launch_bounds__((64 * attn_waves<D, MODE>()), (attn_occupancy<D, MODE>())) void attn_bf16_track_kernel(
+    AttnArgs a) {
     MOBA_RING_ARRAYS(D)
     const unsigned n = *a.defer_count;
     for (unsigned i = wg_x(); i < n; i += a.nwg) {
-        attn_bf16_tile<D, MODE, false, PAD, attn_waves<D>()>(a, a.defer_list[i], sK0, sK1, sK2, sK3, sV0, sV1, sV2, sV3, sFlag);
+        attn_bf16_tile<D, MODE, false, PAD, attn_waves<D, MODE>()>(a, a.defer_list[i], sK0, sK1, sK2, sK3, sV0,
+                                                                  sV1, sV2, sV3, sFlag);
         __syncthreads();
     }
 }
@@ -972,9 +985,9 @@ constexpr unsigned kTrackGrid = 256;
 template <int D, int MODE, bool PAD>
 static void bf16_pair(AttnArgs a, unsigned grid, hipStream_t st) {
     a.nwg = grid;
-    attn_bf16_kernel<D, MODE, PAD><<<grid, 64 * attn_waves<D>(), 0, st>>>(a);
+    attn_bf16_kernel<D, MODE, PAD><<<grid, 64 * attn_waves<D, MODE>(), 0, st>>>(a);
     a.nwg = kTrackGrid;
-    attn_bf16_track_kernel<D, MODE, PAD><<<kTrackGrid, 64 * attn_waves<D>(), 0, st>>>(a);
+    attn_bf16_track_kernel<D, MODE, PAD><<<kTrackGrid, 64 * attn_waves<D, MODE>(), 0, st>>>(a);
 }
 
 template <int MODE>
@@ -1010,6 +1023,7 @@ hipError_t launch_attn_past(const AttnBuffers &bf, const Problem &p, uint64_t ti
 
 hipError_t launch_attn_own(const AttnBuffers &bf, const Problem &p, hipStream_t st) {
     AttnArgs a = make_args(bf, p);
+    a.M = own_tile_rows(p);
     a.ntiles = (unsigned)own_tiles(p);
     a.fuse_merge = merge_in_own_pass(p) ? 1 : 0;
     return attn_launch<kOwn>(a, p, round8(a.ntiles), st);

@@ -108,10 +108,17 @@ hipError_t launch_backward(const BwdBuffers &bb, const Problem &p, uint64_t tile
 // rows for d = 128, 4 x 64 for d = 64), 128 on the fp32 path (two threads a row).
 inline int tile_rows(const Problem &p) { return p.dtype == kBF16 ? 256 : 128; }
 
+// Own-block tiles of the bf16 d = 128 path hold 128 rows (4 waves): two such
+// workgroups share a CU, so one's merge epilogue (bound by HBM) runs beside
+// the other's key loop (bound by the matrix cores).
+inline int own_tile_rows(const Problem &p) {
+    return (p.dtype == kBF16 && p.D == 128) ? 128 : tile_rows(p);
+}
+
 // Tiles of each attention launch (the past-block count is an upper bound).
 inline unsigned long long own_tiles(const Problem &p) {
     return (unsigned long long)p.batch * p.Hkv * ((p.R + p.B - 1) / p.B) * p.G *
-           ((p.B + tile_rows(p) - 1) / tile_rows(p));
+           ((p.B + own_tile_rows(p) - 1) / own_tile_rows(p));
 }
 inline unsigned long long dense_tiles(const Problem &p) {
     return (unsigned long long)p.batch * p.Hq * ((p.S + tile_rows(p) - 1) / tile_rows(p));
