@@ -49,6 +49,7 @@ struct AttnArgs {
     int batch, S, Hq, Hkv, G, B, n, topk, nslot;
     int r0, R;             // query chunk [r0, r0 + R): partial buffers are chunk-local
     int M;                 // query rows per tile
+    int dense_heads;       // DENSE: heads per tile (M / dense_heads tokens of each); else 1
     long long L;           // number of lists
     unsigned ntiles;       // tiles of OWN / DENSE launches
     unsigned nwg;          // workgroups of the launch
@@ -81,8 +82,15 @@ __device__ inline T ld_index(const T *p) {
 
 // This workgroup's tile: past-block launches are sized by an upper bound on
 // the tile count, so their XCD shares come from the count itself.
+// PAST / OWN: consecutive tiles share keys, so each XCD takes a contiguous
+// share.  DENSE: tiles are ordered longest first, so a contiguous share would
+// leave one XCD with all the long tiles; the workgroup index itself deals
+// them round-robin (XCD x gets every 8th tile, longest first), and with the
+// (token range, KV group) order the tiles an XCD runs together read the same
+// keys whenever the group count divides 8.
 __device__ inline unsigned first_tile(const AttnArgs &a, int mode) {
-    return mode == kPast ? xcd_tile_counted(wg_x(), ld_index(a.tile_off + a.L)) : xcd_tile(wg_x(), a.nwg);
+    if (mode == kPast) return xcd_tile_counted(wg_x(), ld_index(a.tile_off + a.L));
+    return mode == kDense ? wg_x() : xcd_tile(wg_x(), a.nwg);
 }
 
 __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, Tile &tl) {
@@ -117,18 +125,21 @@ __device__ inline bool decode_tile(const AttnArgs &a, int mode, unsigned tile, T
         tl.key_begin = i * a.B;
         tl.npast = min(a.topk - 1, i);
     } else {
-        const int ntt = (a.S + a.M - 1) / a.M;
-        const int bh = tile % (a.batch * a.Hq);
-        const int tt = ntt - 1 - (int)(tile / (a.batch * a.Hq));
-        tl.b = bh / a.Hq;
-        tl.h = bh % a.Hq;
+        // M / Gd tokens of Gd heads of one KV group (heads h .. h + Gd - 1), the
+        // latest (heaviest) token ranges first
+        const int hpt = a.dense_heads, TT = a.M / hpt, nhc = a.Hq / hpt;
+        const int ntt = (a.S + TT - 1) / TT;
+        const int bhc = tile % (a.batch * nhc);
+        const int tt = ntt - 1 - (int)(tile / (a.batch * nhc));
+        tl.b = bhc / nhc;
+        tl.h = (bhc % nhc) * hpt;
         tl.g = tl.h / a.G;
-        tl.t0 = tt * a.M;
+        tl.t0 = tt * TT;
         tl.tend = a.S;
         tl.key_begin = 0;
         tl.npast = 0;
     }
-    tl.tmax = min(tl.t0 + a.M, tl.tend) - 1;
+    tl.tmax = min(tl.t0 + a.M / a.dense_heads, tl.tend) - 1;
     tl.nslice = (tl.tmax - tl.key_begin) / 32 + 1;
     return true;
 }
@@ -377,7 +388,9 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
     const __bf16 *__restrict__ kp = static_cast<const __bf16 *>(a.k);
     const __bf16 *__restrict__ vp = static_cast<const __bf16 *>(a.v);
     const int nh = tl.nslice;
-    const int wfirst = tl.t0 + wave * RPW;   // OWN / DENSE: the wave's first row
+    // OWN / DENSE: row r of the tile is token t0 + r mod TT of head h + r / TT
+    const int TT = a.M / a.dense_heads;
+    const int wfirst = tl.t0 + (wave * RPW) % TT;   // the wave's first row (one head per wave)
 
     // this lane's two query rows (column groups g = 0, 1)
     bool rvalid[NG];
@@ -393,9 +406,9 @@ __device__ __forceinline__ void attn_bf16_tile(const AttnArgs &a, unsigned tile,
             h[g] = tl.g * a.G + (int)row_hh(rec);
             slot[g] = (int)row_slot(rec);
         } else {
-            t[g] = tl.t0 + r;
+            t[g] = tl.t0 + r % TT;
             rvalid[g] = t[g] < tl.tend;
-            h[g] = tl.h;
+            h[g] = tl.h + r / TT;
         }
         tq[g] = rvalid[g] ? t[g] : 0x7fffffff;    // padding rows never mask anything
     }
@@ -973,6 +986,7 @@ static AttnArgs make_args(const AttnBuffers &bf, const Problem &p) {
     a.ntiles = 0;
     a.nwg = 0;
     a.M = tile_rows(p);
+    a.dense_heads = 1;
     a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)p.D));
     return a;
 }
@@ -1031,8 +1045,8 @@ hipError_t launch_attn_own(const AttnBuffers &bf, const Problem &p, hipStream_t 
 
 hipError_t launch_attn_dense(const AttnBuffers &bf, const Problem &p, hipStream_t st) {
     AttnArgs a = make_args(bf, p);
-    const unsigned long long ntt = (p.S + a.M - 1) / a.M;
-    a.ntiles = (unsigned)(ntt * p.batch * p.Hq);
+    a.dense_heads = dense_heads(p);
+    a.ntiles = (unsigned)dense_tiles(p);
     return attn_launch<kDense>(a, p, round8(a.ntiles), st);
 }
 

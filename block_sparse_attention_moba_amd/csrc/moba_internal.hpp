@@ -120,8 +120,20 @@ inline unsigned long long own_tiles(const Problem &p) {
     return (unsigned long long)p.batch * p.Hkv * ((p.R + p.B - 1) / p.B) * p.G *
            ((p.B + own_tile_rows(p) - 1) / own_tile_rows(p));
 }
+// Query heads per full-attention tile: the bf16 path puts 256 / Gd tokens of
+// Gd heads of one KV group in a tile, so the key prefix a tile streams serves
+// Gd heads at once; Gd is the largest of 8, 4, 2 that divides the group and
+// keeps every wave's rows inside one head (1 on the fp32 path).
+inline int dense_heads(const Problem &p) {
+    if (p.dtype != kBF16) return 1;
+    const int rpw = p.D == 128 ? 32 : 64;   // rows per wave
+    for (int gd = 8; gd >= 2; gd /= 2)
+        if (p.G % gd == 0 && (tile_rows(p) / gd) % rpw == 0) return gd;
+    return 1;
+}
 inline unsigned long long dense_tiles(const Problem &p) {
-    return (unsigned long long)p.batch * p.Hq * ((p.S + tile_rows(p) - 1) / tile_rows(p));
+    const int gd = dense_heads(p), tt = tile_rows(p) / gd;
+    return (unsigned long long)p.batch * (p.Hq / gd) * ((p.S + tt - 1) / tt);
 }
 
 // Partial-output slots per query row: one per selectable past block, then

@@ -239,6 +239,13 @@ def test_varlen_prefill(cfg, lengths, chunk, dev):
     small("dense-switch-bf16", hq=4, hkv=2, seqlen=1024, block_size=256, topk=4),
     small("dense-switch-fp32-d64", hq=2, hkv=1, seqlen=512, head_dim=64, dtype="fp32",
           block_size=64, topk=9),
+    # tiles of 32 tokens x 8 heads of one KV group, short last block
+    small("dense-switch-gqa8-d128-tail", hq=16, hkv=2, seqlen=1088, block_size=128, topk=9),
+    # tiles of 64 tokens x 4 heads at d = 64, two sequences
+    small("dense-switch-gqa4-d64-b2", batch=2, hq=8, hkv=2, seqlen=1088, head_dim=64,
+          block_size=256, topk=5),
+    # G = 6: 128 tokens x 2 heads per tile, the last token range half full
+    small("dense-switch-gqa6-ragged", hq=12, hkv=2, seqlen=704, block_size=64, topk=11),
 ], ids=lambda c: c.name)
 def test_every_block_selected_is_full_causal_attention(cfg, dev):
     """topk >= n runs the full causal path; the oracle with all blocks is dense causal."""
@@ -254,6 +261,8 @@ def test_every_block_selected_is_full_causal_attention(cfg, dev):
     (small("large-logits-sparse", hq=4, hkv=2, seqlen=1024, block_size=128, topk=3), 32),
     (small("large-logits-block192", hq=2, hkv=1, seqlen=1152, block_size=192, topk=3), 32),
     (small("large-logits-dense", hq=2, hkv=2, seqlen=768, block_size=128, topk=6), 32),
+    (small("large-logits-dense-gqa8", hq=8, hkv=1, seqlen=832, block_size=128, topk=7), 32),
+    (small("mixed-logits-dense-gqa4", hq=8, hkv=2, seqlen=1024, block_size=128, topk=8), 12),
     (small("bounded-logits-to-25", hq=4, hkv=2, seqlen=1024, block_size=128, topk=3), 8),
     (small("mixed-bounded-and-tracked", hq=4, hkv=2, seqlen=1024, block_size=128, topk=3), 12),
 ], ids=lambda c: c.name if hasattr(c, "name") else f"x{c}")
