@@ -70,7 +70,17 @@ extern "C" {
 
 #define MOBA_ABI_VERSION 1
 
-typedef enum {
+/* The enums are int-sized.  In C++ they are declared with int as their
+ * underlying type, so that any int a foreign caller passes (an unknown dtype,
+ * an unknown status code) is a value of the type and is refused or named by
+ * the library rather than being undefined behaviour inside it. */
+#ifdef __cplusplus
+#define MOBA_ENUM_BASE : int
+#else
+#define MOBA_ENUM_BASE
+#endif
+
+typedef enum moba_status_e MOBA_ENUM_BASE {
     MOBA_OK = 0,
     MOBA_ERR_INVALID_ARGUMENT = 1,
     MOBA_ERR_UNSUPPORTED = 2,
@@ -78,7 +88,7 @@ typedef enum {
     MOBA_ERR_HIP = 4
 } moba_status_t;
 
-typedef enum { MOBA_DTYPE_BF16 = 0, MOBA_DTYPE_FP32 = 1 } moba_dtype_t;
+typedef enum moba_dtype_e MOBA_ENUM_BASE { MOBA_DTYPE_BF16 = 0, MOBA_DTYPE_FP32 = 1 } moba_dtype_t;
 
 /* Stages of moba_prefill, in launch order (for moba_prefill_timed). */
 enum {
