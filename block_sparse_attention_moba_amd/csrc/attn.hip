@@ -80,12 +80,12 @@ __device__ inline T ld_index(const T *p) {
     return *(const __attribute__((address_space(4))) T *)p;
 }
 
-// This workgroup's tile: past-block launches are sized by an upper bound on
-// the tile count, so their XCD shares come from the count itself.
-// PAST / OWN: consecutive tiles share keys, so each XCD takes a contiguous
-// share.  DENSE: tiles are ordered longest first, so a contiguous share would
-// leave one XCD with all the long tiles; the workgroup index itself deals
-// them round-robin (XCD x gets every 8th tile, longest first), and with the
+// This workgroup's tile.  PAST / OWN: consecutive tiles share keys, so each
+// XCD takes a contiguous share (past-block launches are sized by an upper
+// bound on the tile count, so their shares come from the count itself).
+// DENSE: tiles are ordered longest first, so a contiguous share would leave
+// one XCD with all the long tiles; the workgroup index itself deals them
+// round-robin (XCD x gets every 8th tile, longest first), and with the
 // (token range, KV group) order the tiles an XCD runs together read the same
 // keys whenever the group count divides 8.
 __device__ inline unsigned first_tile(const AttnArgs &a, int mode) {
