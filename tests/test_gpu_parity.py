@@ -394,6 +394,40 @@ def test_bitwise_deterministic(dev):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("cfg", [
+    small("neighbours-bf16", hq=4, hkv=2, seqlen=2048, block_size=128, topk=4),
+    small("neighbours-fp32-d64", hq=4, hkv=1, seqlen=1024, head_dim=64, dtype="fp32",
+          block_size=64, topk=5),
+], ids=lambda c: c.name)
+def test_row_result_independent_of_tile_neighbours(cfg, dev):
+    """A row's output depends on its own query, K and V only: which other rows
+    share its tiles, and in what order tiles run, must not change a bit of it.
+    Half of the tokens get fresh queries (same distribution), which changes
+    their selections and so the composition and boundaries of every block's
+    row list and of every tile; the other tokens' outputs must be identical."""
+    moba = _moba()
+    log(f"case {cfg.name}")
+    inp = make_inputs(cfg)
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    a = moba.moba_prefill(q, k, v, cfg.block_size, cfg.topk)
+    gen = torch.Generator().manual_seed(4242)
+    redraw = torch.rand(cfg.seqlen, generator=gen) < 0.5          # tokens whose queries change
+    fresh = (torch.randn(q.shape, generator=gen) / cfg.head_dim ** 0.5).to(q.dtype)
+    q2 = q.clone()
+    q2[:, redraw.to(dev)] = fresh.to(dev)[:, redraw.to(dev)]
+    b = moba.moba_prefill(q2, k, v, cfg.block_size, cfg.topk)
+    idx_a = moba.moba_gate(q, k, cfg.block_size, cfg.topk)
+    idx_b = moba.moba_gate(q2, k, cfg.block_size, cfg.topk)
+    torch.cuda.synchronize()
+    keep = ~redraw
+    sel_changed = (idx_a != idx_b).any(dim=-1)[:, :, redraw.to(dev)].float().mean().item()
+    log(f"[{cfg.name}] {int(redraw.sum())} tokens redrawn, {sel_changed:.0%} of their rows "
+        f"select differently")
+    assert sel_changed > 0.1                       # the lists really changed
+    assert torch.equal(idx_a[:, :, keep.to(dev)], idx_b[:, :, keep.to(dev)])
+    assert torch.equal(a[:, keep.to(dev)], b[:, keep.to(dev)])
+
+
 @pytest.mark.timeout(300)
 def test_32k_every_row(dev):
     """The 32K workload: selections and outputs of every row of every head."""
