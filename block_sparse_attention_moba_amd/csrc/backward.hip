@@ -53,11 +53,23 @@ struct BwdArgs {
 };
 
 // LDS rows of D bf16 with their 16-byte chunks XOR-swizzled by the row index,
-// so that both the row reads (one 16-byte chunk per lane, 32 rows) and the
-// transposing reads (4 rows x 4 dims per 16 lanes) spread over the banks.
+// so that both kinds of read spread over the banks:
+//   row reads, one 16-byte chunk per lane: the rows that share banks in one
+//   pass (16 consecutive rows of 256 bytes; the even or the odd ones of 16
+//   rows of 128 bytes) get distinct chunks;
+//   transposing reads, 32 lanes over rows r0 .. r0 + 3 (r0 a multiple of 4)
+//   and four adjacent chunks 4c .. 4c + 3: the rows that share banks land in
+//   different aligned groups of four chunks.
+// (XOR with r mod 16 alone satisfies the first but puts rows r0 .. r0 + 3 of
+// a transposing read on the same four chunks.)
+template <int D>
+__device__ inline int lds_swz(int r) {
+    if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 template <int D>
 __device__ inline int lds_off(int r, int chunk) {
-    return r * D + ((chunk ^ (r & (D / 8 - 1))) << 3);
+    return r * D + ((chunk ^ lds_swz<D>(r)) << 3);
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdArgs a) {
     // slice ends at its last row rounded up to 32 (S is a multiple of 64).
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int rq = (D == 128 ? wave : (wave & 3)) * RPI + lane / CPR;
-    const int pc = ((lane % CPR) ^ (rq & (CPR - 1))) << 3;
+    const int pc = ((lane % CPR) ^ lds_swz<D>(rq)) << 3;
     const size_t rstride = (size_t)a.Hkv * D;
     const size_t kvoff = ((size_t)tl.b * a.S + tl.key_begin + rq) * rstride + (size_t)tl.g * D + pc;
     const __bf16 *srcA = (D == 128 || wave < 4 ? a.k : a.v) + kvoff;   // K (D = 64: K or V)
@@ -493,7 +505,7 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BwdArgs a, int nsub, unsign
     // workspace holds nslot x D values for every (batch, head, token) row.
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);     // scalar copy, for the LDS bases
     const int rq = (D == 128 ? wave : (wave & 3)) * RPI + lane / CPR;
-    const int pc = ((lane % CPR) ^ (rq & (CPR - 1))) << 3;
+    const int pc = ((lane % CPR) ^ lds_swz<D>(rq)) << 3;
     const __bf16 *rowA = (D == 128 || wave < 4 ? a.q : a.dout) + pc;   // Q (D = 64: Q or dO)
     const __bf16 *rowB = a.dout + pc;                                  // dO (D = 128)
     const unsigned rqHq = (unsigned)rq * (unsigned)a.Hq;
