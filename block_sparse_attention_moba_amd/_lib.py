@@ -26,7 +26,7 @@ EXPORTS = ("moba_abi_version", "moba_status_string", "moba_workspace_size", "mob
            "moba_gate", "moba_prefill", "moba_prefill_timed", "moba_workspace_size_chunked",
            "moba_prefill_chunked", "moba_workspace_size_varlen", "moba_prefill_varlen",
            "moba_prefill_lse", "moba_workspace_size_backward", "moba_backward",
-           "moba_prefill_noalloc")
+           "moba_prefill_noalloc", "moba_gate_scores")
 # bytes of moba_prefill_noalloc's scratch array on each GPU (MOBA_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 512 << 20
 
@@ -82,6 +82,8 @@ def lib():
     L.moba_backward.argtypes = [vp] * 9 + [ci] * 8 + [vp, sz, vp]
     L.moba_prefill_noalloc.restype = ci
     L.moba_prefill_noalloc.argtypes = [vp, vp, vp, vp] + [ci] * 8 + [vp]
+    L.moba_gate_scores.restype = ci
+    L.moba_gate_scores.argtypes = [vp, vp, vp] + [ci] * 7 + [vp, sz, vp]
     _lib = L
     return L
 
@@ -291,6 +293,23 @@ def moba_gate(q, k, block_size, topk, workspace=None):
     _check(lib().moba_gate(_ptr(q), _ptr(k), _ptr(idx), b, S, hq, hkv, d, block_size, topk, dt,
                            _ptr(ws), _nbytes(ws), _stream()), "moba_gate")
     return idx
+
+
+def moba_gate_scores(q, k, block_size, workspace=None):
+    """The bf16 gate's scores: fp32 [batch, hq, seqlen, n], NaN for blocks not in a row's past."""
+    _need_cuda(q, k)
+    b, S, hq, d = q.shape
+    hkv = k.shape[2]
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype:
+        raise TypeError("q and k must share a dtype")
+    _, gb = moba_workspace_size(b, S, hq, hkv, d, block_size, 1, dt)
+    ws = _workspace(gb, q.device, workspace)
+    n = -(-S // block_size)
+    scores = torch.empty((b, hq, S, n), dtype=torch.float32, device=q.device)
+    _check(lib().moba_gate_scores(_ptr(q), _ptr(k), _ptr(scores), b, S, hq, hkv, d, block_size, dt,
+                                  _ptr(ws), _nbytes(ws), _stream()), "moba_gate_scores")
+    return scores
 
 
 def moba_prefill(q, k, v, block_size, topk, out=None, workspace=None, stage_events=None,

@@ -656,6 +656,67 @@ static hipError_t gate_kp(const void *q, const float *kbar, int32_t *idx, const 
     return gate_impl<T, D, 32>(q, kbar, idx, p, st);
 }
 
+// The gate scores themselves (for tests of the gate's arithmetic): s_j =
+// q_t . K-bar_j for every past block j < t / B, computed as the bf16 gate
+// kernels compute them (per 16 dimensions the hi product, then the lo
+// product, into one fp32 accumulator); NaN for j >= t / B.  One wave per 32
+// tokens of one head; the block means are read straight from global memory.
+// grid (S / 32, Hq, batch), 64 threads; scores [batch][Hq][S][n].
+template <int D>
+__global__ __launch_bounds__(64) void gate_scores_kernel(const __bf16 *__restrict__ q,
+                                                         const __bf16 *__restrict__ khl,
+                                                         float *__restrict__ scores, int S, int Hq,
+                                                         int Hkv, int G, int B, int n) {
+    constexpr int KD = D / 16;
+    const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
+    const int t0 = blockIdx.x * 32, h = blockIdx.y, b = blockIdx.z, g = h / G;
+    const int t = t0 + col;                          // this lane's query row (S % 64 == 0)
+    bf16x8_t qf[KD];
+    const __bf16 *src = q + (((size_t)b * S + t) * Hq + h) * D + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t *>(src + kk * 16);
+    const __bf16 *kb = khl + ((size_t)b * Hkv + g) * n * 2 * D;
+    const int own = t / B, nch = ((t0 + 31) / B + 31) / 32;
+    float *row = scores + (((size_t)b * Hq + h) * S + t) * n;
+    for (int c = 0; c < nch; ++c) {
+        const int blk = c * 32 + col;                // this lane's A-operand block
+        f32x16_t acc = {};
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+            bf16x8_t ah, al;
+            if (blk < n) {
+                ah = *reinterpret_cast<const bf16x8_t *>(kb + (size_t)blk * 2 * D + kk * 16 + half * 8);
+                al = *reinterpret_cast<const bf16x8_t *>(kb + (size_t)blk * 2 * D + D + kk * 16 + half * 8);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ah[e] = al[e] = (__bf16)0.f;
+            }
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[kk], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[kk], acc, 0, 0, 0);
+        }
+        // lane (col, half) holds blocks 32 c + 8 (i / 4) + 4 half + i % 4 of row col
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int j = c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (j < n) row[j] = j < own ? acc[i] : __builtin_nanf("");
+        }
+    }
+    // blocks past the tile's last own block
+    for (int j = nch * 32 + half; j < n; j += 2) row[j] = __builtin_nanf("");
+}
+
+hipError_t launch_gate_scores(const void *q, const __bf16 *khl, float *scores, const Problem &p,
+                              hipStream_t st) {
+    dim3 grid(p.S / 32, p.Hq, p.batch);
+    if (p.D == 64)
+        gate_scores_kernel<64><<<grid, 64, 0, st>>>(static_cast<const __bf16 *>(q), khl, scores, p.S,
+                                                    p.Hq, p.Hkv, p.G, p.B, p.n);
+    else
+        gate_scores_kernel<128><<<grid, 64, 0, st>>>(static_cast<const __bf16 *>(q), khl, scores, p.S,
+                                                     p.Hq, p.Hkv, p.G, p.B, p.n);
+    return hipGetLastError();
+}
+
 hipError_t launch_gate(const void *q, const float *kbar, const __bf16 *khl, int32_t *idx,
                        const Problem &p, hipStream_t st) {
     if (p.dense) {

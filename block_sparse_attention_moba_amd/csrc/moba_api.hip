@@ -430,6 +430,26 @@ moba_status_t moba_gate(const void *q, const void *k, int32_t *block_idx, int ba
     return hip_status(e);
 }
 
+moba_status_t moba_gate_scores(const void *q, const void *k, float *scores, int batch, int S,
+                               int Hq, int Hkv, int D, int B, moba_dtype_t dt, void *ws,
+                               size_t ws_bytes, void *stream) {
+    Problem p;
+    const moba_status_t rc = make_problem(batch, S, Hq, Hkv, D, B, 1, dt, &p);
+    if (rc != MOBA_OK) return rc;
+    if (!q || !k || !scores || !ws) return MOBA_ERR_INVALID_ARGUMENT;
+    if (p.dtype != kBF16) return MOBA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(scores, 4) || !aligned(ws, kAlign))
+        return MOBA_ERR_UNSUPPORTED;
+    const Layout l = gate_layout(p);
+    if (ws_bytes < l.total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    hipStream_t st = as_stream(stream);
+    char *w = static_cast<char *>(ws);
+    const PoolBuffers pb = pool_buffers(w, l, nullptr);
+    hipError_t e = launch_pool(k, pb, p, st);
+    if (e == hipSuccess) e = launch_gate_scores(q, pb.khl, scores, p, st);
+    return hip_status(e);
+}
+
 moba_status_t moba_prefill(const void *q, const void *k, const void *v, void *out, int batch,
                            int S, int Hq, int Hkv, int D, int B, int topk, moba_dtype_t dt,
                            void *ws, size_t ws_bytes, void *stream) {

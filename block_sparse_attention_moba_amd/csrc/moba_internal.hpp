@@ -64,6 +64,8 @@ struct PoolBuffers {
 hipError_t launch_pool(const void *k, const PoolBuffers &pb, const Problem &p, hipStream_t st);
 hipError_t launch_gate(const void *q, const float *kbar, const __bf16 *khl, int32_t *idx,
                        const Problem &p, hipStream_t st);
+hipError_t launch_gate_scores(const void *q, const __bf16 *khl, float *scores, const Problem &p,
+                              hipStream_t st);
 hipError_t launch_index(const int32_t *idx, uint32_t *cnt, uint32_t *cursor, uint64_t *list_off,
                         uint32_t *tile_off, uint32_t *tile_list, uint64_t tiles_upper,
                         uint64_t *lists, const Problem &p, hipStream_t st);

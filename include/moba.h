@@ -143,6 +143,23 @@ moba_status_t moba_gate(const void *q, const void *k, int32_t *block_idx, int ba
                         void *stream);
 
 /*
+ * The gate scores that moba_gate ranks, for checking the gate's arithmetic:
+ * scores[b][h][t][j] = q[b][t][h] . kbar[b][h / (Hq/Hkv)][j] for every past
+ * block j < t / block_size (the gate of the write-up's first implementation
+ * step, on the block means of the overview, section "技術細節與優勢"), NaN for
+ * j >= t / block_size.  Computed as the bf16 gate computes them: per 16
+ * dimensions the product with the bf16 hi part of the mean, then with the lo
+ * part, into one fp32 accumulator.  bf16 only (fp32 inputs: UNSUPPORTED).
+ * scores: [batch][num_q_heads][seqlen][n] fp32, n = ceil(seqlen / block_size),
+ * 4-byte aligned, caller-owned, fully overwritten.  Workspace: at least
+ * *gate_bytes of moba_workspace_size.  Errors as moba_gate.
+ */
+moba_status_t moba_gate_scores(const void *q, const void *k, float *scores, int batch, int seqlen,
+                               int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                               moba_dtype_t dtype, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
  * Whole MoBA causal prefill forward: out = softmax attention of each query
  * over the tokens t' <= t of its selected blocks.  topk >= n gives exact full
  * causal attention (no gating is run).

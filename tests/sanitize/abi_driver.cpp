@@ -110,6 +110,12 @@ int main() {
     int32_t *idx = static_cast<int32_t *>(at(FAKE + (11ull << 32)));
     EXPECT(moba_gate(nullptr, k, idx, 1, 1024, 2, 2, 64, 128, 3, BF16, ws, big, nullptr) == MOBA_ERR_INVALID_ARGUMENT);
     EXPECT(moba_gate(q, k, idx, 1, 1024, 2, 2, 64, 128, 3, BF16, ws, 8, nullptr) == MOBA_ERR_WORKSPACE_TOO_SMALL);
+    EXPECT(moba_gate_scores(nullptr, k, static_cast<float *>(ws), 1, 1024, 2, 2, 64, 128, BF16, ws, big,
+                            nullptr) == MOBA_ERR_INVALID_ARGUMENT);
+    EXPECT(moba_gate_scores(q, k, static_cast<float *>(o), 1, 1024, 2, 2, 64, 128, F32, ws, big, nullptr) ==
+           MOBA_ERR_UNSUPPORTED);
+    EXPECT(moba_gate_scores(q, k, static_cast<float *>(o), 1, 1024, 2, 2, 64, 128, BF16, ws, 8, nullptr) ==
+           MOBA_ERR_WORKSPACE_TOO_SMALL);
     EXPECT(moba_pool(k, nullptr, 1, 1024, 2, 64, 128, BF16, ws, big, nullptr) == MOBA_ERR_INVALID_ARGUMENT);
     EXPECT(moba_pool(k, static_cast<float *>(ws), 1, 1024, 2, 64, 100, BF16, ws, big, nullptr) ==
            MOBA_ERR_UNSUPPORTED);

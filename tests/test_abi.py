@@ -256,6 +256,21 @@ def test_gate_and_pool_validation():
                        None) == UNS
 
 
+def test_gate_scores_validation():
+    vp = ctypes.c_void_p
+    L = moba.lib()
+    assert L.moba_gate_scores(vp(0), vp(FAKE), vp(FAKE + (1 << 32)), 1, 1024, 2, 2, 64, 128, BF16,
+                              vp(FAKE + (2 << 32)), 1 << 40, None) == INV
+    assert L.moba_gate_scores(vp(FAKE), vp(FAKE), vp(FAKE + (1 << 32)), 1, 1024, 2, 2, 64, 128, F32,
+                              vp(FAKE + (2 << 32)), 1 << 40, None) == UNS     # bf16 only
+    assert L.moba_gate_scores(vp(FAKE), vp(FAKE), vp(FAKE + (1 << 32) + 2), 1, 1024, 2, 2, 64, 128,
+                              BF16, vp(FAKE + (2 << 32)), 1 << 40, None) == UNS
+    assert L.moba_gate_scores(vp(FAKE), vp(FAKE), vp(FAKE + (1 << 32)), 1, 1024, 2, 2, 64, 128, BF16,
+                              vp(FAKE + (2 << 32)), 8, None) == WS
+    assert L.moba_gate_scores(vp(FAKE), vp(FAKE), vp(FAKE + (1 << 32)), 1, 1000, 2, 2, 64, 128, BF16,
+                              vp(FAKE + (2 << 32)), 1 << 40, None) == UNS     # S % 64
+
+
 def test_python_binding_refuses_host_tensors():
     import torch
     q = torch.zeros(1, 128, 2, 64, dtype=torch.bfloat16)

@@ -148,6 +148,7 @@ def test_prefill_every_row(cfg, dev):
     out, idx = run_gpu(cfg, inp, dev)
     rows = oracle.all_rows(cfg.batch, cfg.hq, cfg.seqlen)
     check_rows(cfg, host_arrays(inp), out, idx, rows)
+    check_hull(cfg, out, idx, inp["v"])
 
 
 def test_pool_matches_oracle(dev):
@@ -395,6 +396,50 @@ def test_bitwise_deterministic(dev):
 
 
 @pytest.mark.parametrize("cfg", [
+    small("scores-gqa4-d128-tail", hq=8, hkv=2, seqlen=1088, block_size=64, topk=4),
+    small("scores-d64-b2", batch=2, hq=4, hkv=2, seqlen=640, head_dim=64, block_size=64, topk=3),
+    small("scores-320-blocks", hq=2, hkv=1, seqlen=64 * 320, block_size=64, topk=12, planted=12),
+], ids=lambda c: c.name)
+def test_gate_scores_within_error_bound(cfg, dev):
+    """The bf16 gate's fp32 scores (moba_gate_scores) against the oracle's fp64
+    scores on every (row, past block): |s_gpu - s| <= 4 2^-16 |q| |kbar_j|.  The
+    hi/lo split of a block mean leaves at most 2^-17 |kbar| per element, the
+    fp32 accumulation of the 2d products about as much again; 4 2^-16 keeps a
+    factor of 4.  NaN exactly where the block is not in the row's past.  And
+    these are the scores the gate ranks: the top-k taken from them on the host
+    (ties to the smaller block) equals moba_gate's selection on every row."""
+    moba = _moba()
+    b, S, hq, hkv, d, B, topk = dims(cfg)
+    n, G = -(-S // B), hq // hkv
+    inp = make_inputs(cfg)
+    q, k = inp["q"].to(dev), inp["k"].to(dev)
+    got = moba.moba_gate_scores(q, k, B).cpu().numpy().reshape(-1, n)
+    idx = moba.moba_gate(q, k, B, topk).cpu().numpy().reshape(-1, topk)
+    qa, ka, va, code = host_arrays(inp)
+    kbar = oracle.pool(ka, code, b, S, hkv, d, B)
+    rows = oracle.all_rows(b, hq, S)
+    _, _, ref = oracle.gate(qa, code, kbar, b, S, hq, hkv, d, B, topk, rows, want_scores=True)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    qn = np.linalg.norm(inp["q"].double().permute(0, 2, 1, 3).reshape(-1, d).numpy(), axis=1)
+    kn = np.linalg.norm(np.asarray(kbar).reshape(b, hkv, n, d), axis=3)        # [b, hkv, n]
+    bound = 4 * 2.0 ** -16 * qn[:, None] * kn[rows[:, 0], rows[:, 1] // G]
+    past = ~np.isnan(ref)
+    ratio = np.abs(got - ref)[past] / bound[past]
+    log(f"[{cfg.name}] {past.sum()} scores: max |error| / bound {ratio.max():.3g}, "
+        f"median {np.median(ratio):.3g}")
+    assert ratio.max() <= 1.0
+    # the selection the gate makes from exactly these values
+    want = np.full_like(idx, -1)
+    for r in range(len(rows)):
+        own = int(rows[r, 2]) // B
+        s = got[r, :own]
+        order = np.lexsort((np.arange(own), -s))[:min(topk - 1, own)]
+        sel = sorted(order.tolist()) + [own]
+        want[r, :len(sel)] = sel
+    assert np.array_equal(want, idx)
+
+
+@pytest.mark.parametrize("cfg", [
     small("neighbours-bf16", hq=4, hkv=2, seqlen=2048, block_size=128, topk=4),
     small("neighbours-fp32-d64", hq=4, hkv=1, seqlen=1024, head_dim=64, dtype="fp32",
           block_size=64, topk=5),
@@ -439,6 +484,51 @@ def test_32k_every_row(dev):
     check_rows(cfg, host_arrays(inp), out, idx, rows)
 
 
+def check_hull(cfg, out, idx, v, tag=""):
+    """Every output element lies between the smallest and the largest value of
+    its dimension over the V rows its query attends: the softmax weights are a
+    convex combination.  A property that holds at any size, checked here for
+    every row on the GPU (torch reductions; nothing of the library's kernels).
+    The attended rows are the causal prefix of the own block and every row of
+    the selected past blocks (idx).  bf16: the output is the round-to-nearest
+    of a value in that range and the range ends are bf16 values, so the bound
+    holds exactly; 2^-9 of the range end is allowed for fp32 rounding before
+    the final rounding."""
+    b, S, hq, hkv, d, B, topk = dims(cfg)
+    G, n = hq // hkv, -(-S // B)
+    vf = v.float()
+    if n * B > S:   # a short last block: repeat its last token (inside the block's range)
+        vf = torch.cat([vf, vf[:, -1:].expand(b, n * B - S, hkv, d)], 1)
+    vb = vf.view(b, n, B, hkv, d)
+    bmin, bmax = vb.amin(2), vb.amax(2)                          # [b, n, hkv, d]
+    pmin = torch.cummin(vb, 2).values.view(b, n * B, hkv, d)     # own-block prefixes
+    pmax = torch.cummax(vb, 2).values.view(b, n * B, hkv, d)
+    del vf, vb
+    bi = torch.arange(b, device=out.device)[:, None]
+    worst, CH = 0.0, 1 << 16
+    for h in range(hq):
+        g = h // G
+        bmn, bmx = bmin[:, :, g], bmax[:, :, g]
+        for t0 in range(0, S, CH):
+            t1 = min(S, t0 + CH)
+            own = torch.arange(t0, t1, device=out.device) // B
+            lo, hi = pmin[:, t0:t1, g], pmax[:, t0:t1, g]
+            sel = idx[:, h, t0:t1, :].long()
+            for c in range(topk):
+                j = sel[..., c]
+                past = ((j >= 0) & (j != own))[..., None]
+                jj = j.clamp(min=0)
+                lo = torch.where(past, torch.minimum(lo, bmn[bi, jj]), lo)
+                hi = torch.where(past, torch.maximum(hi, bmx[bi, jj]), hi)
+            o = out[:, t0:t1, h].float()
+            tol = 2.0 ** -9 * torch.maximum(lo.abs(), hi.abs())
+            excess = torch.maximum(lo - o, o - hi) / torch.clamp(tol, min=1e-30)
+            worst = max(worst, excess.max().item())
+    log(f"[{tag or cfg.name}] hull bound on every row: worst excess {worst:.3g} x tolerance "
+        f"(<= 0: inside)")
+    assert worst <= 1.0
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("which", [3, 4], ids=["128k", "1m"])
 def test_full_size(which, dev):
@@ -446,7 +536,8 @@ def test_full_size(which, dev):
     Selections: 128K every row of every head (4.2M rows); 1M every row of the
     first and last KV head groups (2 x 4 heads x 1M rows), the oracle run per
     group (groups are independent in every stage).  Outputs: the stratified
-    row sample of every head."""
+    row sample of every head against the oracle, and every row of every head
+    against the hull bound."""
     cfg = CONFIGS[which]
     moba = _moba()
     log(f"case {cfg.name}: generating on GPU")
@@ -455,6 +546,7 @@ def test_full_size(which, dev):
     out = moba.moba_prefill(q, k, v, cfg.block_size, cfg.topk)
     idx = moba.moba_gate(q, k, cfg.block_size, cfg.topk)
     torch.cuda.synchronize()
+    check_hull(cfg, out, idx, v)
     log(f"case {cfg.name}: GPU done, copying to host")
     host = {x: inp[x].cpu() for x in ("q", "k", "v")}
     out_h, idx_h = out.cpu(), idx.cpu()
