@@ -404,23 +404,30 @@ __global__ __launch_bounds__(64 * kGateMaxWaves, (gate_sp_waves<KP, NCH>())) voi
         const long long k1 = ((long long)(pair + 1) * n32 - w + grid - 1) / grid;
         stage(pair);
         const int b = pair / a.Hkv, g = pair % a.Hkv, h = g * a.G + hh;
+        auto item_t0 = [&](long long k) { return a.r0 + (n32 - 1 - (int)((w + k * grid) % n32)) * 32; };
+        // Q of the item's 32 rows; the next item's is loaded as soon as this
+        // item's last product has been issued, so that its latency overlaps the
+        // rest of this item (the last insertions, the merge, the emission)
+        bf16x8_t qf[KD];
+        auto load_q = [&](long long k) {
+            const __bf16 *src = a.q + (((size_t)b * a.S + item_t0(k) + col) * a.Hq + h) * D + half * 8;
+    #pragma unroll
+            for (int kk = 0; kk < KD; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t *>(src + kk * 16);
+        };
+        auto needs_q = [&](long long k) { return k < k1 && item_t0(k) / a.B > a.topk - 1; };
+        if (needs_q(k0 + tg)) load_q(k0 + tg);
         for (long long k = k0 + tg; k < k1; k += a.TW) {
-            const int tt32 = n32 - 1 - (int)((w + k * grid) % n32);
-            const int t0 = a.r0 + tt32 * 32;
+            const int t0 = item_t0(k);
             const int own = t0 / a.B;                      // all 32 rows share a block
+            const bool pref = needs_q(k + a.TW);
             if (own <= a.topk - 1) {
+                if (pref) load_q(k + a.TW);
                 // every past block is selected: blocks 0 .. own - 1, the own block, then -1
                 for (int e = lane; e < 32 * a.topk; e += 64) {
                     const int c = e % a.topk;
                     stage_row[e] = c < own ? c : (c == own ? own : -1);
                 }
             } else {
-                bf16x8_t qf[KD];
-                {
-                    const __bf16 *src = a.q + (((size_t)b * a.S + t0 + col) * a.Hq + h) * D + half * 8;
-    #pragma unroll
-                    for (int kk = 0; kk < KD; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t *>(src + kk * 16);
-                }
                 const int nchw = (own + 31) / 32;          // chunks of past blocks (wave-uniform)
                 f32x16_t sc[NCH];
                 float lst[KP];
@@ -428,10 +435,12 @@ __global__ __launch_bounds__(64 * kGateMaxWaves, (gate_sp_waves<KP, NCH>())) voi
                 for (int p = 0; p < KP; ++p) lst[p] = -INFINITY;
                 // the matrix cores compute chunk c + 1 while the vector unit inserts chunk c
                 sc[0] = chunk_scores(0, qf);
+                if (nchw == 1 && pref) load_q(k + a.TW);
     #pragma unroll
                 for (int c = 0; c < NCH; ++c) {
                     if (c + 1 < NCH && c + 1 < nchw) {
                         sc[c + 1] = chunk_scores(c + 1, qf);
+                        if (c + 2 == nchw && pref) load_q(k + a.TW);
     #pragma unroll
                         for (int i = 0; i < 16; ++i) value_insert<KP>(lst, sc[c][i]);
                     } else if (c + 1 == nchw) {
@@ -677,7 +686,10 @@ __global__ __launch_bounds__(64) void gate_scores_kernel(const __bf16 *__restric
     for (int kk = 0; kk < KD; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t *>(src + kk * 16);
     const __bf16 *kb = khl + ((size_t)b * Hkv + g) * n * 2 * D;
     const int own = t / B, nch = ((t0 + 31) / B + 31) / 32;
-    float *row = scores + (((size_t)b * Hq + h) * S + t) * n;
+    // stored as bit patterns: this file is built with NaNs ruled out of its
+    // floating-point arithmetic, so the quiet NaN is never a float value here
+    constexpr uint32_t kNaN = 0x7fc00000u;
+    uint32_t *row = reinterpret_cast<uint32_t *>(scores) + (((size_t)b * Hq + h) * S + t) * n;
     for (int c = 0; c < nch; ++c) {
         const int blk = c * 32 + col;                // this lane's A-operand block
         f32x16_t acc = {};
@@ -698,11 +710,11 @@ __global__ __launch_bounds__(64) void gate_scores_kernel(const __bf16 *__restric
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int j = c * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (j < n) row[j] = j < own ? acc[i] : __builtin_nanf("");
+            if (j < n) row[j] = j < own ? __float_as_uint(acc[i]) : kNaN;
         }
     }
     // blocks past the tile's last own block
-    for (int j = nch * 32 + half; j < n; j += 2) row[j] = __builtin_nanf("");
+    for (int j = nch * 32 + half; j < n; j += 2) row[j] = kNaN;
 }
 
 hipError_t launch_gate_scores(const void *q, const __bf16 *khl, float *scores, const Problem &p,
