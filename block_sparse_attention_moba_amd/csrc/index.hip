@@ -6,16 +6,17 @@
 // packed (token, head-in-group, slot) records and the attention kernel
 // gathers the query rows it names.
 //
-//   count   : per-workgroup LDS histogram of the selected past blocks, then
+//   count   : per-workgroup LDS histogram of the selected past blocks (a
+//             workgroup: 256 tokens of the G query heads of a KV group), then
 //             one global atomic per (workgroup, block).
 //   scan    : one workgroup; exclusive scan of the list lengths (row offsets)
 //             and of their tile counts (tile offsets); clears the cursors.
 //   tile map: the list index of every attention tile (a binary search over
 //             the tile offsets, once per tile), so the attention kernel finds
 //             its list with one load instead of a chain of dependent ones.
-//   scatter : LDS atomics give each selection a rank inside its workgroup,
-//             one global atomic per (workgroup, block) reserves a range, and
-//             each record is written to its slot of the list.
+//   scatter : the same histogram again, one global atomic per (workgroup,
+//             block) reserves a range of the list, and a second walk over the
+//             selections places each record in it (an LDS atomic per record).
 // The order of records inside a list depends on scheduling; no result does,
 // because every row's attention is computed independently of its neighbours.
 #include "moba_internal.hpp"
@@ -27,31 +28,61 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p,
     if (i < n) p[i] = 0u;
 }
 
-// Query rows of the chunk [r0, r0 + R); idx rows are chunk-local.
-// grid (ceil(R / 256), Hq, batch), 256 threads.
+// The selections of a workgroup's rows are read as one contiguous span of
+// the block-index array (rows of one head are consecutive, topk entries
+// each), 16 bytes per lane: the span starts at a multiple of 256 rows of a
+// 256-byte aligned buffer and holds a multiple of 64 rows, so every 16-byte
+// piece is aligned and whole.  Entry e of the span is slot e mod topk of row
+// e / topk; the quotient comes from a multiply by ceil(2^32 / topk), exact
+// for e * topk < 2^32 (here e < 256 * topk and topk <= 32; topk 1 has no
+// past slot and is never launched, but its quotient is e itself).
+// Tokens per workgroup of the count and scatter kernels.
+constexpr int kIdxRows = 256;
+__device__ inline uint32_t div_magic(int topk) {
+    return (uint32_t)((0x100000000ull + (unsigned)topk - 1) / (unsigned)topk);
+}
+__device__ inline int span_row(int e, uint32_t mt, int topk) {
+    return topk == 1 ? e : (int)__umulhi((uint32_t)e, mt);
+}
+
+// Query rows of the chunk [r0, r0 + R); idx rows are chunk-local.  A
+// workgroup takes kIdxRows tokens of every query head of one KV group, the heads
+// whose selections feed the same lists, so that one global atomic per
+// (workgroup, block) covers G heads.
+// grid (ceil(R / kIdxRows), Hkv, batch), 256 threads.
 __global__ __launch_bounds__(256) void count_kernel(const int32_t *__restrict__ idx,
                                                     uint32_t *__restrict__ cnt, int r0, int R,
                                                     int Hq, int Hkv, int G, int B, int n,
                                                     int topk) {
     __shared__ uint32_t hist[kHistMax];
-    const int h = blockIdx.y, b = blockIdx.z, g = h / G;
-    const int t = r0 + blockIdx.x * 256 + threadIdx.x;
-    const int jend = min(r0 + (int)blockIdx.x * 256 + 255, r0 + R - 1) / B;
+    __shared__ int sown[kIdxRows];
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int tb = r0 + blockIdx.x * kIdxRows, nrow = min(kIdxRows, r0 + R - tb);
+    const int jend = (tb + nrow - 1) / B;          // the last row's own block
     const bool use_lds = n <= kHistMax;
     uint32_t *gcnt = cnt + ((size_t)b * Hkv + g) * n;
-    if (use_lds) {
+    for (int r = threadIdx.x; r < nrow; r += 256) sown[r] = (tb + r) / B;
+    if (use_lds)
         for (int j = threadIdx.x; j < jend; j += 256) hist[j] = 0u;
-        __syncthreads();
-    }
-    if (t < r0 + R) {
-        const int own = t / B;
-        const int np = min(topk - 1, own);
-        const int32_t *row = idx + (((size_t)b * Hq + h) * R + (t - r0)) * topk;
-        for (int c = 0; c < np; ++c) {
-            const int j = row[c];
-            if ((unsigned)j >= (unsigned)own) continue;   // never produced by the gate
-            if (use_lds) atomicAdd(&hist[j], 1u);
-            else atomicAdd(&gcnt[j], 1u);
+    __syncthreads();
+    const uint32_t mt = div_magic(topk);
+    const int nq = nrow * topk / 4;
+    for (int hh = 0; hh < G; ++hh) {
+        const int4 *span = reinterpret_cast<const int4 *>(
+            idx + (((size_t)b * Hq + g * G + hh) * R + (tb - r0)) * topk);
+        for (int q = threadIdx.x; q < nq; q += 256) {
+            const int4 v = span[q];
+            const int jj[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = 4 * q + u, r = span_row(e, mt, topk), c = e - r * topk;
+                const int own = sown[r], j = jj[u];
+                // past slots only; an index at or past the own block is never produced by the gate
+                if (c < min(topk - 1, own) && (unsigned)j < (unsigned)own) {
+                    if (use_lds) atomicAdd(&hist[j], 1u);
+                    else atomicAdd(&gcnt[j], 1u);
+                }
+            }
         }
     }
     if (use_lds) {
@@ -135,7 +166,11 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const uint32_t *__restric
     tile_list[t] = (uint32_t)lo;
 }
 
-// grid (ceil(R / 256), Hq, batch), 256 threads.
+// grid (ceil(R / kIdxRows), Hkv, batch), 256 threads; the rows of count_kernel.
+// With the LDS histogram: (1) count the workgroup's selections per block,
+// (2) reserve each block's range of its list with one global atomic, (3) walk
+// the selections again, an LDS atomic giving each its place in the range.
+// Beyond kHistMax blocks every selection reserves its own place globally.
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict__ idx,
                                                       uint32_t *__restrict__ cursor,
                                                       const uint64_t *__restrict__ list_off,
@@ -144,44 +179,53 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict_
                                                       int topk) {
     __shared__ uint32_t hist[kHistMax];
     __shared__ uint32_t base[kHistMax];
-    const int h = blockIdx.y, b = blockIdx.z, g = h / G, hh = h % G;
-    const int t = r0 + blockIdx.x * 256 + threadIdx.x;
-    const bool in = t < r0 + R;
-    const int jend = min(r0 + (int)blockIdx.x * 256 + 255, r0 + R - 1) / B;
+    __shared__ int sown[kIdxRows];
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int tb = r0 + blockIdx.x * kIdxRows, nrow = min(kIdxRows, r0 + R - tb);
+    const int jend = (tb + nrow - 1) / B;
     const bool use_lds = n <= kHistMax;
     const size_t lbase = ((size_t)b * Hkv + g) * n;
-    if (use_lds) {
+    for (int r = threadIdx.x; r < nrow; r += 256) sown[r] = (tb + r) / B;
+    if (use_lds)
         for (int j = threadIdx.x; j < jend; j += 256) hist[j] = 0u;
-        __syncthreads();
-    }
-    const int own = in ? t / B : 0;
-    const int np = in ? min(topk - 1, own) : 0;
-    const int32_t *row = idx + (((size_t)b * Hq + h) * R + (in ? t - r0 : 0)) * topk;
-    uint32_t rank[kMaxPast];
+    __syncthreads();
+    const uint32_t mt = div_magic(topk);
+    const int nq = nrow * topk / 4;
+    // walk every past selection of the workgroup's rows: f(j, token, head in group, slot)
+    auto walk = [&](auto &&f) {
+        for (int hh = 0; hh < G; ++hh) {
+            const int4 *span = reinterpret_cast<const int4 *>(
+                idx + (((size_t)b * Hq + g * G + hh) * R + (tb - r0)) * topk);
+            for (int q = threadIdx.x; q < nq; q += 256) {
+                const int4 v = span[q];
+                const int jj[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int c = 0; c < kMaxPast; ++c) {
-        rank[c] = 0u;
-        if (c < np) {
-            const int j = row[c];
-            if ((unsigned)j >= (unsigned)own) continue;
-            rank[c] = use_lds ? atomicAdd(&hist[j], 1u) : atomicAdd(&cursor[lbase + j], 1u);
+                for (int u = 0; u < 4; ++u) {
+                    const int e = 4 * q + u, r = span_row(e, mt, topk), c = e - r * topk;
+                    const int own = sown[r], j = jj[u];
+                    if (c < min(topk - 1, own) && (unsigned)j < (unsigned)own) f(j, tb + r, hh, c);
+                }
+            }
         }
+    };
+    if (!use_lds) {
+        walk([&](int j, int t, int hh, int c) {
+            const uint32_t rank = atomicAdd(&cursor[lbase + j], 1u);
+            lists[list_off[lbase + j] + rank] = pack_row((uint32_t)t, (uint32_t)hh, (uint32_t)c);
+        });
+        return;
     }
-    if (use_lds) {
-        __syncthreads();
-        for (int j = threadIdx.x; j < jend; j += 256)
-            if (hist[j]) base[j] = atomicAdd(&cursor[lbase + j], hist[j]);
-        __syncthreads();
+    walk([&](int j, int, int, int) { atomicAdd(&hist[j], 1u); });
+    __syncthreads();
+    for (int j = threadIdx.x; j < jend; j += 256) {
+        if (hist[j]) base[j] = atomicAdd(&cursor[lbase + j], hist[j]);
+        hist[j] = 0u;
     }
-#pragma unroll
-    for (int c = 0; c < kMaxPast; ++c) {
-        if (c < np) {
-            const int j = row[c];
-            if ((unsigned)j >= (unsigned)own) continue;
-            const uint64_t pos = list_off[lbase + j] + (use_lds ? base[j] : 0u) + rank[c];
-            lists[pos] = pack_row((uint32_t)t, (uint32_t)hh, (uint32_t)c);
-        }
-    }
+    __syncthreads();
+    walk([&](int j, int t, int hh, int c) {
+        const uint32_t rank = atomicAdd(&hist[j], 1u);
+        lists[list_off[lbase + j] + base[j] + rank] = pack_row((uint32_t)t, (uint32_t)hh, (uint32_t)c);
+    });
 }
 
 hipError_t launch_index(const int32_t *idx, uint32_t *cnt, uint32_t *cursor, uint64_t *list_off,
@@ -189,7 +233,7 @@ hipError_t launch_index(const int32_t *idx, uint32_t *cnt, uint32_t *cursor, uin
                         uint64_t *lists, const Problem &p, hipStream_t st) {
     const long long L = (long long)p.batch * p.Hkv * p.n;
     fill_u32_kernel<<<(unsigned)((L + 255) / 256), 256, 0, st>>>(cnt, L);
-    dim3 grid((p.R + 255) / 256, p.Hq, p.batch);
+    dim3 grid((p.R + kIdxRows - 1) / kIdxRows, p.Hkv, p.batch);
     count_kernel<<<grid, 256, 0, st>>>(idx, cnt, p.r0, p.R, p.Hq, p.Hkv, p.G, p.B, p.n, p.topk);
     scan_kernel<<<1, 1024, 0, st>>>(cnt, cursor, list_off, tile_off, L, tile_rows(p));
     if (tiles_upper > 0)
