@@ -168,8 +168,10 @@ __global__ __launch_bounds__(256) void tile_map_kernel(const uint32_t *__restric
 
 // grid (ceil(R / kIdxRows), Hkv, batch), 256 threads; the rows of count_kernel.
 // With the LDS histogram: (1) count the workgroup's selections per block,
-// (2) reserve each block's range of its list with one global atomic, (3) walk
-// the selections again, an LDS atomic giving each its place in the range.
+// (2) reserve each block's range of its list with one global atomic and keep
+// the range's start (the list's offset included) in LDS, (3) walk the
+// selections again, a 64-bit LDS atomic on that start giving each record its
+// address in the list array.
 // Beyond kHistMax blocks every selection reserves its own place globally.
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict__ idx,
                                                       uint32_t *__restrict__ cursor,
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict_
                                                       int Hq, int Hkv, int G, int B, int n,
                                                       int topk) {
     __shared__ uint32_t hist[kHistMax];
-    __shared__ uint32_t base[kHistMax];
+    __shared__ unsigned long long dst[kHistMax];
     __shared__ int sown[kIdxRows];
     const int g = blockIdx.y, b = blockIdx.z;
     const int tb = r0 + blockIdx.x * kIdxRows, nrow = min(kIdxRows, r0 + R - tb);
@@ -217,14 +219,12 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t *__restrict_
     }
     walk([&](int j, int, int, int) { atomicAdd(&hist[j], 1u); });
     __syncthreads();
-    for (int j = threadIdx.x; j < jend; j += 256) {
-        if (hist[j]) base[j] = atomicAdd(&cursor[lbase + j], hist[j]);
-        hist[j] = 0u;
-    }
+    for (int j = threadIdx.x; j < jend; j += 256)
+        if (hist[j]) dst[j] = list_off[lbase + j] + atomicAdd(&cursor[lbase + j], hist[j]);
     __syncthreads();
     walk([&](int j, int t, int hh, int c) {
-        const uint32_t rank = atomicAdd(&hist[j], 1u);
-        lists[list_off[lbase + j] + base[j] + rank] = pack_row((uint32_t)t, (uint32_t)hh, (uint32_t)c);
+        const unsigned long long pos = atomicAdd(&dst[j], 1ull);
+        lists[pos] = pack_row((uint32_t)t, (uint32_t)hh, (uint32_t)c);
     });
 }
 
