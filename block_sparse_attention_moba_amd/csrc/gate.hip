@@ -404,7 +404,10 @@ __global__ __launch_bounds__(64 * kGateMaxWaves, (gate_sp_waves<KP, NCH>())) voi
         const long long k1 = ((long long)(pair + 1) * n32 - w + grid - 1) / grid;
         stage(pair);
         const int b = pair / a.Hkv, g = pair % a.Hkv, h = g * a.G + hh;
-        auto item_t0 = [&](long long k) { return a.r0 + (n32 - 1 - (int)((w + k * grid) % n32)) * 32; };
+        // first token of item k of this pair (k0 <= k < k1: item w + k grid lies in the pair)
+        auto item_t0 = [&](long long k) {
+            return a.r0 + (n32 - 1 - (int)(w + k * grid - (long long)pair * n32)) * 32;
+        };
         // Q of the item's 32 rows; the next item's is loaded as soon as this
         // item's last product has been issued, so that its latency overlaps the
         // rest of this item (the last insertions, the merge, the emission)
