@@ -407,7 +407,42 @@ def total_work(cfg):
     return scored * cfg.hq * cfg.batch, int(round(pairs))
 
 
-def cpu_baseline(cfg, host, mode):
+def cpu_prepare(cfg, host, mode):
+    """Host-side inputs of one CPU-oracle leg: the oracle's views of Q, K and V
+    and the row sets.  Built on the calling thread, between GPU timings, so
+    that the leg's own thread runs only oracle calls (which release the
+    interpreter lock) and never holds up the launches of a timed region."""
+    import numpy as np
+    import oracle
+    from synth import sample_rows, to_oracle_array
+    qa, code = to_oracle_array(host["q"])
+    ka, _ = to_oracle_array(host["k"])
+    va, _ = to_oracle_array(host["v"])
+    b, S, hq, hkv = cfg.batch, cfg.seqlen, cfg.hq, cfg.hkv
+    # 8192 random rows on top of the strata (about 13K rows at 128K and 1M):
+    # a few hundred rows leave the oracle's per-call costs in the extrapolation
+    n_random = 8192
+    if mode == "full":
+        sample = gate_rows = oracle.all_rows(b, hq, S)
+    else:
+        sample = sample_rows(cfg, tile=32, n_random=n_random)
+        if mode == "group":
+            # every row of the first KV group's query heads, and the sample rows,
+            # in (b, h, t) order without repeats
+            key = lambda r: (r[:, 0] * hq + r[:, 1]) * S + r[:, 2]
+            keys = np.unique(np.concatenate([key(oracle.all_rows(b, hq // hkv, S)), key(sample)]))
+            gate_rows = np.stack([keys // (hq * S), (keys // S) % hq, keys % S], axis=1)
+        else:
+            gate_rows = oracle.all_rows(b, hq, S)
+    # where each sample row sits among the gate rows (both in (b, h, t) order)
+    key = lambda r: (r[:, 0] * hq + r[:, 1]) * S + r[:, 2]
+    pos = None if mode == "full" else np.searchsorted(key(gate_rows), key(sample))
+    return {"qa": qa, "ka": ka, "va": va, "code": code, "sample": sample, "gate_rows": gate_rows,
+            "sample_pos": pos, "scored_g": row_work(cfg, gate_rows)[0],
+            "pairs_s": row_work(cfg, sample)[1]}
+
+
+def cpu_baseline(cfg, prep, mode):
     """The fp64 oracle as it stands on the host cores, timed on one workload.
 
     mode "full": pool, gate and attention of every row.
@@ -421,39 +456,21 @@ def cpu_baseline(cfg, host, mode):
       of the same row sample, extrapolated by attended pairs.  Sized for 10-30 s of oracle time on 16 cores at 1M,
       where the full gate alone takes about a minute.
     """
-    import numpy as np
     import oracle
-    from synth import sample_rows, to_oracle_array
-    qa, code = to_oracle_array(host["q"])
-    ka, _ = to_oracle_array(host["k"])
-    va, _ = to_oracle_array(host["v"])
+    qa, ka, va, code = prep["qa"], prep["ka"], prep["va"], prep["code"]
+    sample, gate_rows = prep["sample"], prep["gate_rows"]
     b, S, hq, hkv, d, B, k = (cfg.batch, cfg.seqlen, cfg.hq, cfg.hkv, cfg.head_dim,
                               cfg.block_size, cfg.topk)
-    all_rows = oracle.all_rows(b, hq, S)
-    # 8192 random rows on top of the strata (about 13K rows at 128K and 1M):
-    # a few hundred rows leave the oracle's per-call costs in the extrapolation
-    n_random = 8192
-    sample = all_rows if mode == "full" else sample_rows(cfg, tile=32, n_random=n_random)
-    if mode == "group":
-        group = all_rows[all_rows[:, 1] < hq // hkv]
-        gate_rows = np.unique(np.concatenate([group, sample]), axis=0)
-    else:
-        gate_rows = all_rows if mode in ("full", "gate") else sample
     t0 = time.perf_counter()
     kbar = oracle.pool(ka, code, b, S, hkv, d, B)
     t1 = time.perf_counter()
     idx, _, _ = oracle.gate(qa, code, kbar, b, S, hq, hkv, d, B, k, gate_rows)
     t2 = time.perf_counter()
-    if mode == "full":
-        idx_s = idx
-    else:                         # gate rows and sample rows are both in (b, h, t) order
-        key = lambda r: (r[:, 0] * hq + r[:, 1]) * S + r[:, 2]
-        idx_s = idx[np.searchsorted(key(gate_rows), key(sample))]
+    idx_s = idx if mode == "full" else idx[prep["sample_pos"]]
     oracle.attend(qa, ka, va, code, b, S, hq, hkv, d, B, k, sample, idx_s)
     t3 = time.perf_counter()
     scored_all, pairs_all = total_work(cfg)
-    scored_g, _ = row_work(cfg, gate_rows)
-    _, pairs_s = row_work(cfg, sample)
+    scored_g, pairs_s = prep["scored_g"], prep["pairs_s"]
     t_gate = (t2 - t1) * scored_all / max(scored_g, 1)
     t_attn = (t3 - t2) if mode == "full" else (t3 - t2) * pairs_all / max(pairs_s, 1)
     est = (t1 - t0) + t_gate + t_attn
@@ -487,8 +504,13 @@ class CpuLegs:
         self.thread = None
 
     def add(self, key, cfg, host, mode):
+        try:
+            prep = cpu_prepare(cfg, host, mode)       # on this thread, between GPU timings
+        except Exception as e:                         # reported in the line, never fatal
+            self.errors[key] = repr(e)
+            return
         with self.lock:
-            self.jobs.append((key, cfg, host, mode))
+            self.jobs.append((key, cfg, prep, mode))
         if self.thread is None:
             self.thread = threading.Thread(target=self._run, daemon=True)
             self.thread.start()
@@ -499,10 +521,10 @@ class CpuLegs:
                 if not self.jobs:
                     self.thread = None
                     return
-                key, cfg, host, mode = self.jobs.pop(0)
+                key, cfg, prep, mode = self.jobs.pop(0)
             try:
                 log(f"cpu oracle: {key} ({mode}) started")
-                self.results[key] = cpu_baseline(cfg, host, mode)
+                self.results[key] = cpu_baseline(cfg, prep, mode)
                 log(f"cpu oracle: {key} done in {self.results[key]['measured_s']:.1f} s")
             except Exception as e:                     # reported in the line, never fatal
                 self.errors[key] = repr(e)
