@@ -28,16 +28,19 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p,
     if (i < n) p[i] = 0u;
 }
 
-// The selections of a workgroup's rows are read as one contiguous span of
-// the block-index array (rows of one head are consecutive, topk entries
-// each), 16 bytes per lane: the span starts at a multiple of 256 rows of a
-// 256-byte aligned buffer and holds a multiple of 64 rows, so every 16-byte
-// piece is aligned and whole.  Entry e of the span is slot e mod topk of row
-// e / topk; the quotient comes from a multiply by ceil(2^32 / topk), exact
-// for e * topk < 2^32 (here e < 256 * topk and topk <= 32; topk 1 has no
-// past slot and is never launched, but its quotient is e itself).
 // Tokens per workgroup of the count and scatter kernels.
 constexpr int kIdxRows = 256;
+
+// The selections of a workgroup's rows are read, per query head, as one
+// contiguous span of the block-index array (a head's rows are consecutive,
+// topk entries each), 16 bytes per lane.  The buffer is 256-byte aligned, a
+// head's rows start at a multiple of R rows (R a multiple of 64), the span at
+// a multiple of kIdxRows rows after that, and it holds a multiple of 64 rows,
+// so every 16-byte piece is aligned and whole.  Entry e of the span is slot
+// e mod topk of row e / topk; the quotient comes from a multiply by
+// ceil(2^32 / topk), exact for e * topk < 2^32 (here e < kIdxRows * topk and
+// topk <= 32; topk 1 has no past slot and is never launched, but its
+// quotient is e itself).
 __device__ inline uint32_t div_magic(int topk) {
     return (uint32_t)((0x100000000ull + (unsigned)topk - 1) / (unsigned)topk);
 }
