@@ -453,8 +453,9 @@ def cpu_baseline(cfg, prep, mode):
     mode "group": pool of every block; the gate of every row of the first KV
       group's query heads plus the sample rows, extrapolated by scored blocks
       (the groups are alike: the same rows, the same block counts); attention
-      of the same row sample, extrapolated by attended pairs.  Sized for 10-30 s of oracle time on 16 cores at 1M,
-      where the full gate alone takes about a minute.
+      of the same row sample, extrapolated by attended pairs.  Sized for 10-30 s
+      of oracle time on 16 cores at 1M, where the full gate alone takes about
+      30 s (3.6 s per KV group) and would bring the leg to about 45 s.
     """
     import oracle
     qa, ka, va, code = prep["qa"], prep["ka"], prep["va"], prep["code"]
